@@ -1,0 +1,110 @@
+/*
+ * fa.h -- C ABI of libfa.so, the gfx950 (MI355X) FlashAttention forward pass.
+ *
+ * Operation.  For each batch b and head h, with Q, K, V the [N, d] slices at
+ * (b, h) and X^ the exact value an input element stands for:
+ *
+ *   S   = scale * Q^ K^T                      (scores; never stored)
+ *   S_ij = -inf for j > i when causal != 0    (lower triangle, diagonal kept)
+ *   P   = softmax of each row of S
+ *   O   = P V^                                (written to o)
+ *   lse_i = ln(sum_j exp(S_ij))               (written to lse)
+ *
+ * The order scale -> mask -> softmax -> weighted sum is the fused attention
+ * sequence of page "FlashAttention与TensorRT 10集成", section "算子融合的极致
+ * 优化", item 2; computing it in on-chip tiles so that the N x N matrix never
+ * reaches device memory is the block decomposition of that page's section
+ * "FlashAttention的技术革命" and the "0 MB (重计算)" attention row of the
+ * Flash Attention 2 memory table on page "Optimization Flash Attention 基准测试".
+ * The causal flag is the one in the tuning dict of page "从RTX 3090到H100：
+ * FlashAttention在NVIDIA各代GPU架构上的性能全景分析", section 3.2.  The online
+ * softmax and the lse output are not on the pages: lse is the natural-log
+ * logsumexp of each score row (scale included), what a backward pass needs to
+ * recompute P.
+ *
+ * Layout.  q, k, v, o are dense row-major [B, H, N, d] arrays, d innermost
+ * (element (b,h,n,c) at offset ((b*H + h)*N + n)*d + c).  lse is a dense
+ * float32 [B, H, N] array.  All pointers are device pointers.
+ *
+ * Ownership.  The caller allocates and owns every buffer.  The library
+ * allocates no device or host memory, keeps no mutable global state and may be
+ * called from several host threads at once.  Work is enqueued on `stream` (a
+ * hipStream_t; NULL is the null stream) and the call returns without waiting.
+ *
+ * Errors.  Every entry point returns FA_OK (0) or a negative FA_ERR_* code
+ * and never throws.  All argument checks run before any HIP call, so a
+ * rejected call enqueues nothing.  A fault inside the kernel surfaces as a HIP
+ * error at the caller's next synchronisation of `stream`.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FA_VERSION 100 /* major * 10000 + minor * 100 + patch: 0.1.0 */
+
+/* Storage format of q, k, v. */
+typedef enum {
+  FA_DTYPE_F16 = 0,      /* IEEE binary16; o is binary16 */
+  FA_DTYPE_BF16 = 1,     /* bfloat16; o is bfloat16 */
+  FA_DTYPE_FP8_E4M3 = 2  /* OCP FP8 E4M3 codes (max 448, no inf); o is bfloat16 */
+} fa_dtype;
+
+/* Return codes. */
+enum {
+  FA_OK = 0,
+  FA_ERR_NULL_PTR = -1, /* q, k, v, o or lse is NULL */
+  FA_ERR_SHAPE = -2,    /* B, H or N < 1, a slice of 2 GiB or more, or too many tiles */
+  FA_ERR_HEADDIM = -3,  /* d is not 64 or 128 */
+  FA_ERR_DTYPE = -4,    /* dtype is not an fa_dtype value */
+  FA_ERR_SCALE = -5,    /* scale or a descale is NaN or infinite */
+  FA_ERR_ALIGN = -6,    /* q, k, v or o not 16-byte aligned, or lse not 4-byte aligned */
+  FA_ERR_ALIAS = -7,    /* o or lse overlaps an input, or o overlaps lse */
+  FA_ERR_HIP = -8       /* the kernel launch reported a HIP error */
+};
+
+/*
+ * fa_fwd -- attention forward over [B, H, N, d] tensors of one dtype.
+ *
+ *   q, k, v  inputs, `dtype` elements, read only.
+ *   o        output [B, H, N, d]: binary16 for F16, bfloat16 for BF16 and
+ *            FP8_E4M3; rounded to nearest even from float32.
+ *   lse      output [B, H, N] float32, natural-log logsumexp of each score row.
+ *   B, H, N  batch, heads, sequence length (queries and keys alike), each >= 1.
+ *            Any N is accepted: a tail shorter than a tile is masked, not padded.
+ *   d        head dimension, 64 or 128.
+ *   scale    multiplies Q K^T; any finite value (0 gives a uniform average).
+ *   causal   nonzero: query i sees keys 0..i only.
+ *   dtype    an fa_dtype value.  FA_DTYPE_FP8_E4M3 here means descales of 1.
+ *   stream   hipStream_t to enqueue on, or NULL.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int H, int N, int d, float scale, int causal, int dtype,
+           void* stream);
+
+/*
+ * fa_fwd_fp8 -- fa_fwd for OCP FP8 E4M3 inputs with one float32 descale per
+ * tensor: the value of an element is code * descale (FP8 attention is the
+ * "Flash Attn 3 (FP8)" column of the H100 80GB table on page "Optimization
+ * Flash Attention 基准测试"; per-tensor scaling is this library's reading).
+ * S = scale * q_descale * k_descale * (Qcode Kcode^T); O = softmax(S) *
+ * (Vcode * v_descale), written as bfloat16.  The probabilities enter the
+ * second matrix product as E4M3 codes of P * 2^8.  Descales must be finite.
+ */
+int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int H, int N, int d, float scale, int causal,
+               float q_descale, float k_descale, float v_descale, void* stream);
+
+/* Static description of a return code; never NULL. */
+const char* fa_strerror(int code);
+
+/* FA_VERSION of the built library. */
+int fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

@@ -1,0 +1,115 @@
+"""ctypes binding of libfa.so: argument marshalling only.
+
+``fa_fwd``, ``fa_fwd_fp8``, ``fa_strerror`` and ``fa_version`` take the same
+arguments as the C functions declared in ``include/fa.h`` (device pointers as
+Python ints, the stream as a ``hipStream_t`` int or None).  ``fwd`` allocates
+O and lse with torch on the inputs' device and calls ``fa_fwd`` /
+``fa_fwd_fp8`` on torch's current stream.  Every step of the computation runs
+in the library's HIP kernels; if the library is missing or fails to load, the
+call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # imported first: libfa.so then binds to the HIP runtime torch loaded
+
+FA_DTYPE_F16 = 0
+FA_DTYPE_BF16 = 1
+FA_DTYPE_FP8_E4M3 = 2
+
+_LIB = None
+_HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+class FaError(RuntimeError):
+    """A nonzero return code from libfa.so."""
+
+    def __init__(self, code: int, where: str = "fa_fwd"):
+        self.code = code
+        super().__init__(f"{where} returned {code}: {fa_strerror(code) if _LIB else 'library not loaded'}")
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, "libfa.so")
+
+
+def load() -> ctypes.CDLL:
+    """Load libfa.so once; raise if it has not been built."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'`")
+    lib = ctypes.CDLL(path)
+    vp, ci, cf = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, cf, ci, ci, vp]
+    lib.fa_fwd.restype = ci
+    lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, cf, ci, cf, cf, cf, vp]
+    lib.fa_fwd_fp8.restype = ci
+    lib.fa_strerror.argtypes = [ci]
+    lib.fa_strerror.restype = ctypes.c_char_p
+    lib.fa_version.argtypes = []
+    lib.fa_version.restype = ci
+    _LIB = lib
+    return lib
+
+
+def fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, stream) -> int:
+    return load().fa_fwd(q, k, v, o, lse, B, H, N, d, scale, int(causal), dtype, stream)
+
+
+def fa_fwd_fp8(q, k, v, o, lse, B, H, N, d, scale, causal, q_descale, k_descale, v_descale, stream) -> int:
+    return load().fa_fwd_fp8(q, k, v, o, lse, B, H, N, d, scale, int(causal), q_descale, k_descale, v_descale, stream)
+
+
+def fa_strerror(code: int) -> str:
+    return load().fa_strerror(code).decode()
+
+
+def fa_version() -> int:
+    return load().fa_version()
+
+
+_TORCH_DTYPES = {torch.float16: FA_DTYPE_F16, torch.bfloat16: FA_DTYPE_BF16, torch.float8_e4m3fn: FA_DTYPE_FP8_E4M3}
+
+
+def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: float, causal: bool = False, *,
+        descale=(1.0, 1.0, 1.0), out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+        stream: torch.cuda.Stream | None = None):
+    """Attention forward on [B, H, N, d] device tensors; returns (O, lse).
+
+    fp8 inputs are ``torch.float8_e4m3fn`` (or uint8 codes) with per-tensor
+    ``descale = (q, k, v)``; their O is bfloat16.
+    """
+    if q.dtype == torch.uint8:
+        q, k, v = (t.view(torch.float8_e4m3fn) for t in (q, k, v))
+    if q.dtype not in _TORCH_DTYPES or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError(f"unsupported dtypes {q.dtype}, {k.dtype}, {v.dtype}")
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError(f"q, k, v must share one [B, H, N, d] shape, got {tuple(q.shape)}, {tuple(k.shape)}, {tuple(v.shape)}")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k, v must be contiguous")
+    B, H, N, d = q.shape
+    dt = _TORCH_DTYPES[q.dtype]
+    o_dtype = torch.bfloat16 if dt == FA_DTYPE_FP8_E4M3 else q.dtype
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=o_dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if out.dtype != o_dtype or lse.dtype != torch.float32:
+        raise TypeError("out/lse dtype mismatch")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    s = stream.cuda_stream
+    if dt == FA_DTYPE_FP8_E4M3:
+        rc = fa_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                        B, H, N, d, float(scale), causal, float(descale[0]), float(descale[1]), float(descale[2]), s)
+    else:
+        rc = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                    B, H, N, d, float(scale), causal, dt, s)
+    if rc != 0:
+        raise FaError(rc)
+    return out, lse
