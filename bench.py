@@ -1,0 +1,228 @@
+"""Benchmark of the attention forward pass on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+
+Prints ONE JSON line.  A step is one ``fa_fwd`` call (the whole forward pass:
+Q tile load, K/V streaming, Q K^T, mask, online softmax, P V, epilogue) on
+B=8, H=32, N=1024, d=64 binary16 inputs, non-causal, scale 1/8, drawn i.i.d.
+N(0,1) from seed 0.  Inputs are resident in device memory before the timed
+region; K steps are timed with HIP events on the stream the kernel runs on,
+between two device synchronisations.
+
+Throughput is 4*B*H*N^2*d FLOP per step (halved for causal) / time.  The line
+also carries the sequence-length sweep N = 512..8192 at B=8, H=32, d=64 (the
+shape of the benchmark page's forward-time tables), the fraction of the dense
+fp16 matrix-core peak, HBM traffic from committed rocprofv3 counters when they
+were taken on the current kernel source, and the CPU oracle timed on a bounded
+sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "fp8": 5000.0}  # MI355X dense matrix-core peaks
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_f16_b8h32n1024d64_traffic.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "io_aware_attention_fwd_amd", "csrc", f) for f in ("fa_fwd.hip", "fa_launch.h")]
+
+
+def flops(B, H, N, d, causal):
+    f = 4.0 * B * H * N * N * d
+    return f / 2 if causal else f
+
+
+def algorithmic_bytes(B, H, N, d, in_bytes, out_bytes):
+    # Q, K, V read once, O written once, lse written once
+    return (3 * in_bytes + out_bytes) * B * H * N * d + 4 * B * H * N
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def time_calls(fn, warmup, steps, stream):
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        fn()
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps  # ms per call
+
+
+def make_call(B, H, N, d, dtype, causal, scale, seed=0):
+    import torch
+
+    from io_aware_attention_fwd_amd import _lib, gen
+
+    x = gen.make(B, H, N, d, dtype, seed=seed)
+    tdt = {"f16": torch.float16, "bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn}[dtype]
+
+    def dev(a):
+        if dtype == "bf16":
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        if dtype == "fp8":
+            return torch.from_numpy(a).view(torch.float8_e4m3fn).cuda()
+        return torch.from_numpy(a).cuda()
+
+    q, k, v = dev(x.q), dev(x.k), dev(x.v)
+    o = torch.empty((B, H, N, d), dtype=torch.bfloat16 if dtype == "fp8" else tdt, device="cuda")
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    s = stream.cuda_stream
+    ds = x.descale
+    dt = {"f16": _lib.FA_DTYPE_F16, "bf16": _lib.FA_DTYPE_BF16, "fp8": _lib.FA_DTYPE_FP8_E4M3}[dtype]
+    qp, kp, vp, op, lp = q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr()
+    lib = _lib.load()
+
+    if dtype == "fp8":
+        def call():
+            rc = lib.fa_fwd_fp8(qp, kp, vp, op, lp, B, H, N, d, scale, int(causal), ds["q"], ds["k"], ds["v"], s)
+            if rc:
+                raise _lib.FaError(rc)
+    else:
+        def call():
+            rc = lib.fa_fwd(qp, kp, vp, op, lp, B, H, N, d, scale, int(causal), dt, s)
+            if rc:
+                raise _lib.FaError(rc)
+    return call, stream, (x, q, k, v, o, lse)
+
+
+def cpu_baseline(x, causal, scale, budget_s):
+    """The float64 oracle on as many (b, h) slices of ``x`` as fit in ``budget_s`` seconds."""
+    import oracle
+
+    B, H, N, d = x.shape
+    dtype = x.dtype
+    try:
+        from threadpoolctl import threadpool_info
+
+        cores = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        cores = None
+    done, t0 = 0, time.perf_counter()
+    while True:
+        b, h = divmod(done, H)
+        qkv = [oracle.dequantize(a[b, h], dtype, x.descale[n]) for a, n in ((x.q, "q"), (x.k, "k"), (x.v, "v"))]
+        oracle.attention_slice(qkv[0], qkv[1], qkv[2], scale, causal)
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or done >= B * H:
+            break
+    per_slice = el / done
+    full_s = per_slice * B * H
+    tflops = flops(B, H, N, d, causal) / full_s / 1e12
+    return {"value": tflops, "unit": "TFLOPS", "cores": cores, "kind": "oracle",
+            "sample": f"{done} of {B * H} (b,h) slices of N={N}, d={d} ({dtype} inputs, float64 math) timed in "
+                      f"{el:.1f} s; full workload extrapolated to {full_s:.1f} s ({full_s * 1e3:.0f} ms per step)"}
+
+
+def load_traffic(per_launch_flops_ms):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if current."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-sweep", action="store_true", help="skip the N=512..8192 sweep")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the CPU baseline")
+    ap.add_argument("--copy-calib-mib", type=int, default=0,
+                    help="also run one device copy of this many MiB (reference kernel for HBM counters)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the forward pass has no multi-GPU path in this library)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+
+    B, H, N, d, dtype, causal, scale = 8, 32, 1024, 64, "f16", False, 1.0 / 8
+    call, stream, keep = make_call(B, H, N, d, dtype, causal, scale)
+    if args.copy_calib_mib:
+        n = args.copy_calib_mib * 2 ** 20 // 4
+        a = torch.ones(n, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+    ms = time_calls(call, args.warmup, args.steps, stream)
+    fl = flops(B, H, N, d, causal)
+    tflops = fl / (ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[dtype]
+    algo_bytes = algorithmic_bytes(B, H, N, d, 2, 2)
+
+    sweep = []
+    if not args.no_sweep:
+        for n in (512, 1024, 2048, 4096, 8192):
+            c2, st2, keep2 = make_call(B, H, n, d, dtype, False, scale)
+            reps = 20 if n >= 4096 else 50
+            m2 = time_calls(c2, 5, reps, st2)
+            t2 = flops(B, H, n, d, False) / (m2 * 1e-3) / 1e12
+            sweep.append({"N": n, "ms": round(m2, 4), "tflops": round(t2, 1), "frac_of_peak": round(t2 / peak, 4)})
+            del keep2
+            torch.cuda.empty_cache()
+
+    traffic = load_traffic(None)
+    line = {
+        "metric": "attention fwd TFLOPS + ms at B=8,H=32,d=64,N=512..8192; % of MFMA peak",
+        "value": round(tflops, 2),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic: i.i.d. N(0,1) inputs from seed 0, stored as binary16",
+        "config": {"workload": "attention forward B=8 H=32 N=1024 d=64 f16 non-causal scale=1/8",
+                   "B": B, "H": H, "N": N, "d": d, "causal": causal},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(tflops / peak, 4), "traffic": traffic,
+                     "algorithmic_bytes_per_launch": algo_bytes,
+                     "algorithmic_hbm_gbs": round(algo_bytes / (ms * 1e-3) / 1e9, 1)},
+        "sweep": sweep,
+    }
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(keep[0], causal, scale, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

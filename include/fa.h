@@ -89,9 +89,11 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  * tensor: the value of an element is code * descale (FP8 attention is the
  * "Flash Attn 3 (FP8)" column of the H100 80GB table on page "Optimization
  * Flash Attention 基准测试"; per-tensor scaling is this library's reading).
- * S = scale * q_descale * k_descale * (Qcode Kcode^T); O = softmax(S) *
- * (Vcode * v_descale), written as bfloat16.  The probabilities enter the
- * second matrix product as E4M3 codes of P * 2^8.  Descales must be finite.
+ * S = scale * q_descale * k_descale * (Qcode Kcode^T) is formed by the fp8
+ * matrix cores with float32 accumulation; O = softmax(S) * (Vcode * v_descale)
+ * is formed in bfloat16 (V codes widen exactly to bfloat16, probabilities are
+ * rounded to bfloat16) with float32 accumulation and written as bfloat16.
+ * Descales must be finite.
  */
 int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
                int B, int H, int N, int d, float scale, int causal,

@@ -1,0 +1,504 @@
+// FlashAttention forward for gfx950 (MI355X, CDNA4).
+//
+// One workgroup owns BR = NW * QW consecutive query rows of one (batch, head)
+// slice and streams that slice's keys and values through LDS in tiles of BC
+// rows, so the N x N score matrix only ever exists one BC-wide tile at a time,
+// in registers (the block decomposition into on-chip tiles of page
+// "FlashAttention与TensorRT 10集成", section "FlashAttention的技术革命"; the
+// fused scale -> mask -> softmax -> weighted-sum sequence of its section
+// "算子融合的极致优化").  Each row keeps a reference maximum and a running sum
+// so that partial results are rescaled when a later tile raises the maximum
+// (online softmax; not on the pages, the standard exact formulation).
+//
+// Decomposition (every product is a 32 x 32 matrix-core block):
+//   * NW waves per workgroup, QW = 32 * QB query rows per wave.
+//   * Scores are computed transposed, S^T = K Q^T: A = 32 keys read from LDS,
+//     B = 32 of the wave's queries, held in registers for the whole kernel.
+//     In the accumulator layout each lane then owns one query per 32-row
+//     block (lane % 32) and 16 of the block's keys, so row max and row sum
+//     are lane-local plus one exchange between the two half-waves.  With
+//     QB = 2 every K operand read from LDS feeds two instructions.
+//   * O^T = V^T P^T: B = the probabilities taken straight from the score
+//     accumulators (converted to 16 bits in place, no data movement), A = V^T
+//     read from the row-major V tile with the transposing LDS reads of gfx950
+//     (ds_read_b64_tr_b16, or ds_read_b64_tr_b8 for fp8 values, which are then
+//     widened exactly to bfloat16).
+//   * K and V tiles go HBM -> LDS with buffer loads that write LDS directly
+//     (no registers, out-of-range rows read as zero), double buffered: tile
+//     t+1 is in flight while tile t is computed; one barrier per tile.
+//   * The 16-byte chunks of each LDS row are XOR-swizzled by row.
+//   * Rescaling is lazy and exact: the reference maximum of a row only moves
+//     when a tile's maximum exceeds it by more than 2^8 in the exp2 domain,
+//     so probabilities stay below 256 and the accumulators are rescaled a few
+//     times per row instead of once per tile.
+//   * Causal: tiles right of a wave's last row are skipped; tiles that cross
+//     the diagonal (and the ragged last tile) are masked element-wise.
+//   * exp is v_exp_f32 (exp2) with scale * log2(e) folded into one fma.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "fa_launch.h"
+
+namespace fa {
+namespace {
+
+typedef uint32_t u32;
+typedef u32 u32x4 __attribute__((ext_vector_type(4)));
+typedef u32 u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr float kLn2 = 0.69314718055994531f;
+constexpr float kRescaleThreshold = 8.0f;  // log2 of the largest probability allowed before rescaling
+constexpr u32 kRsrcWord3 = 0x00020000u;    // raw buffer, 32-bit data format, range-checked
+
+// ---------------------------------------------------------------- dtype traits
+struct TrF16 {
+  static constexpr bool kFp8 = false;
+  static constexpr int kEK = 2;  // bytes per Q/K element
+  static constexpr int kEV = 2;  // bytes per V element
+  static constexpr bool kPvBf16 = false;
+};
+struct TrBF16 {
+  static constexpr bool kFp8 = false;
+  static constexpr int kEK = 2;
+  static constexpr int kEV = 2;
+  static constexpr bool kPvBf16 = true;
+};
+struct TrFP8 {
+  static constexpr bool kFp8 = true;
+  static constexpr int kEK = 1;
+  static constexpr int kEV = 1;
+  static constexpr bool kPvBf16 = true;  // P V in bfloat16 with V widened exactly
+};
+
+__device__ __forceinline__ f32x16 mfma16(u32x4 a, u32x4 b, f32x16 c, bool bf16) {
+  if (bf16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+                                                   0, 0);
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c) {
+  // operand format code 0 = E4M3 for both; zero scale operands leave them unscaled
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// Two floats -> one packed 16-bit pair, round to nearest even (one
+// v_cvt_pk_f16_f32 / v_cvt_pk_bf16_f32 on gfx950).
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+template <bool BF16>
+__device__ __forceinline__ u32 pack_p(float lo, float hi) {
+  const f32x2 x = {lo, hi};
+  if (BF16) return __builtin_bit_cast(u32, __builtin_convertvector(x, bf16x2));
+  return __builtin_bit_cast(u32, __builtin_convertvector(x, f16x2));
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, u32 bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, (int)kRsrcWord3);
+}
+
+// 16 bytes per lane from a buffer straight into LDS: lane L of the wave writes
+// lds_block + 16 * L; an out-of-range offset writes zeros.  (Kept in a device
+// function: in a lambda the host pass would see the builtin too.)
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rsrc, char* lds_block, int voffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)lds_block, 16, voffset, 0, 0, 0);
+}
+
+__device__ __forceinline__ u32x4 lds_read_b128(const char* smem, u32 off) {
+  return *reinterpret_cast<const u32x4*>(smem + off);
+}
+
+__device__ __forceinline__ u32x2 lds_read_tr16(const char* smem, u32 off) {
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(smem + off)));
+}
+
+__device__ __forceinline__ u32x2 lds_read_tr8(const char* smem, u32 off) {
+  typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(smem + off)));
+}
+
+// Workgroup id -> logical tile id such that consecutive logical ids run on the
+// same XCD (hardware hands workgroups to the 8 XCDs round-robin).  Consecutive
+// logical ids are query tiles of one (batch, head), so that slice's K and V
+// are fetched once into that XCD's L2 and reused by its other query tiles.
+__device__ __forceinline__ int xcd_remap(int wg, int total) {
+  constexpr int kXcd = 8;
+  const int xcd = wg % kXcd, pos = wg / kXcd;
+  const int per = total / kXcd, rem = total % kXcd;
+  return xcd < rem ? xcd * (per + 1) + pos : rem * (per + 1) + (xcd - rem) * per + pos;
+}
+
+// XOR swizzle of the 16-byte chunks of LDS row r (chunks per row = CPR).
+template <int CPR>
+__device__ __forceinline__ int swz(int r) {
+  constexpr int kMask = CPR >= 8 ? 7 : CPR - 1;
+  return (r ^ (r >> 3)) & kMask;
+}
+
+template <class Tr, int D, int QW, int NW, int BC>
+struct Shape {
+  static constexpr int kQB = QW / 32;         // 32-query blocks per wave
+  static constexpr int kKB = BC / 32;         // 32-key blocks per tile
+  static constexpr int kDB = D / 32;          // 32-wide blocks of the head dimension
+  static constexpr int kBR = NW * QW;         // query rows per workgroup
+  static constexpr int kRK = D * Tr::kEK;     // bytes per K row
+  static constexpr int kRV = D * Tr::kEV;     // bytes per V row
+  static constexpr int kCK = kRK / 16;        // 16-byte chunks per K row
+  static constexpr int kCV = kRV / 16;
+  static constexpr int kSK = BC * kRK;        // bytes per K stage
+  static constexpr int kSV = BC * kRV;
+  static constexpr int kBlkK = kSK / 1024;    // 1 KiB direct-load blocks per K stage
+  static constexpr int kBlkV = kSV / 1024;
+  static constexpr int kQSteps = Tr::kFp8 ? D / 64 : D / 16;  // QK instructions per 32x32 block
+  static_assert(kSK % 1024 == 0 && kSV % 1024 == 0, "stage must be whole 1 KiB blocks");
+};
+
+}  // namespace
+
+// The kernel template has external linkage so that every instantiation's
+// host-side launch stub is emitted.
+template <class Tr, int D, bool CAUSAL, int QW, int NW, int BC>
+__global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(FwdParams p) {
+  using S = Shape<Tr, D, QW, NW, BC>;
+  constexpr bool kBf = Tr::kPvBf16;
+  __shared__ __attribute__((aligned(1024))) char lds_k0[S::kSK];
+  __shared__ __attribute__((aligned(1024))) char lds_k1[S::kSK];
+  __shared__ __attribute__((aligned(1024))) char lds_v0[S::kSV];
+  __shared__ __attribute__((aligned(1024))) char lds_v1[S::kSV];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int half = lane >> 5;
+  const int l32 = lane & 31;
+
+  const int tile = xcd_remap(blockIdx.x, p.total_wg);
+  const int bh = tile / p.n_qtiles;
+  int qt = tile - bh * p.n_qtiles;
+  if (CAUSAL) qt = p.n_qtiles - 1 - qt;  // longest rows first
+  const int N = p.N;
+  const int q0 = qt * S::kBR;
+  const int qw0 = q0 + wave * QW;  // first query row of this wave
+
+  const u32 slice_k = (u32)N * S::kRK;
+  const u32 slice_v = (u32)N * S::kRV;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc((const char*)p.q + (size_t)bh * slice_k, slice_k);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc((const char*)p.k + (size_t)bh * slice_k, slice_k);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc((const char*)p.v + (size_t)bh * slice_v, slice_v);
+
+  // ---- Q operands, kept in registers.  Lane (half, l32) of query block qb
+  // holds row qw0 + 32*qb + l32; k-group `half` of each instruction step.
+  u32x4 q16[S::kQB][Tr::kFp8 ? 1 : S::kQSteps];
+  i32x8 q8[S::kQB][Tr::kFp8 ? S::kQSteps : 1];
+#pragma unroll
+  for (int qb = 0; qb < S::kQB; ++qb) {
+    const int row = qw0 + 32 * qb + l32;
+    if constexpr (Tr::kFp8) {
+#pragma unroll
+      for (int s = 0; s < S::kQSteps; ++s) {
+        const int off = row * S::kRK + 64 * s + 32 * half;
+        const u32x4 x0 = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
+        const u32x4 x1 = __builtin_amdgcn_raw_buffer_load_b128(rq, off + 16, 0, 0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          q8[qb][s][e] = (int)((x0[e] ^ p.q_xor) & p.q_and);
+          q8[qb][s][4 + e] = (int)((x1[e] ^ p.q_xor) & p.q_and);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < S::kQSteps; ++s) {
+        u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rq, row * S::kRK + (16 * s + 8 * half) * 2, 0, 0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = (x[e] ^ p.q_xor) & p.q_and;
+        q16[qb][s] = x;
+      }
+    }
+  }
+
+  const int n_all = (N + BC - 1) / BC;
+  const int n_kv = CAUSAL ? min(n_all, (q0 + S::kBR - 1) / BC + 1) : n_all;
+
+  // ---- direct HBM -> LDS tile loads.  Lane L of a 1 KiB block instruction
+  // writes LDS granule 64*blk + L; it fetches the logical chunk that the
+  // swizzle places there.
+  auto issue_tile = [&](int kt, char* dk, char* dv) {
+    const int k0 = kt * BC;
+#pragma unroll
+    for (int j = 0; j < (S::kBlkK + NW - 1) / NW; ++j) {
+      const int blk = wave + j * NW;
+      if (blk < S::kBlkK) {
+        const int g = blk * 64 + lane;
+        const int r = g / S::kCK, pc = g % S::kCK;
+        const int lc = pc ^ swz<S::kCK>(r);
+        load_lds16(rk, dk + blk * 1024, (k0 + r) * S::kRK + lc * 16);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < (S::kBlkV + NW - 1) / NW; ++j) {
+      const int blk = wave + j * NW;
+      if (blk < S::kBlkV) {
+        const int g = blk * 64 + lane;
+        const int r = g / S::kCV, pc = g % S::kCV;
+        const int lc = pc ^ swz<S::kCV>(r);
+        load_lds16(rv, dv + blk * 1024, (k0 + r) * S::kRV + lc * 16);
+      }
+    }
+  };
+
+  f32x16 oacc[S::kDB][S::kQB];
+#pragma unroll
+  for (int db = 0; db < S::kDB; ++db)
+#pragma unroll
+    for (int qb = 0; qb < S::kQB; ++qb) oacc[db][qb] = f32x16{};
+  float mref[S::kQB], lsum[S::kQB];  // reference max (exp2 domain) and this half-wave's running sum
+#pragma unroll
+  for (int qb = 0; qb < S::kQB; ++qb) {
+    mref[qb] = -INFINITY;
+    lsum[qb] = 0.f;
+  }
+  const float c = p.c;
+
+  auto compute = [&](int kt, const char* lk, const char* lv) {
+    const int k0 = kt * BC;
+    // ---- S^T = K Q^T
+    f32x16 sacc[S::kKB][S::kQB];
+#pragma unroll
+    for (int kb = 0; kb < S::kKB; ++kb) {
+#pragma unroll
+      for (int qb = 0; qb < S::kQB; ++qb) sacc[kb][qb] = f32x16{};
+      const int r = kb * 32 + l32;
+      const int sw = swz<S::kCK>(r);
+#pragma unroll
+      for (int s = 0; s < S::kQSteps; ++s) {
+        if constexpr (Tr::kFp8) {
+          const u32x4 a0 = lds_read_b128(lk, (r * S::kCK + ((4 * s + 2 * half) ^ sw)) * 16);
+          const u32x4 a1 = lds_read_b128(lk, (r * S::kCK + ((4 * s + 2 * half + 1) ^ sw)) * 16);
+          const i32x8 a = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
+                           (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+#pragma unroll
+          for (int qb = 0; qb < S::kQB; ++qb) sacc[kb][qb] = mfma_fp8(a, q8[qb][s], sacc[kb][qb]);
+        } else {
+          const u32x4 a = lds_read_b128(lk, (r * S::kCK + ((2 * s + half) ^ sw)) * 16);
+#pragma unroll
+          for (int qb = 0; qb < S::kQB; ++qb) sacc[kb][qb] = mfma16(a, q16[qb][s], sacc[kb][qb], kBf);
+        }
+      }
+    }
+
+    // ---- mask keys past N and (causal) keys after the query
+    const bool need_mask = (k0 + BC > N) || (CAUSAL && k0 + BC - 1 > qw0);
+    if (need_mask) {
+#pragma unroll
+      for (int qb = 0; qb < S::kQB; ++qb) {
+        const int qi = qw0 + 32 * qb + l32;
+        const int lim = CAUSAL ? min(qi, N - 1) : N - 1;  // last visible key
+#pragma unroll
+        for (int kb = 0; kb < S::kKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+            if (key > lim) sacc[kb][qb][r] = -INFINITY;
+          }
+      }
+    }
+
+    // ---- online softmax with lazy rescaling
+    float mx[S::kQB];
+    bool grow = false;
+#pragma unroll
+    for (int qb = 0; qb < S::kQB; ++qb) {
+      float m = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < S::kKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) m = fmaxf(m, sacc[kb][qb][r]);
+      m = fmaxf(m, __shfl_xor(m, 32));
+      mx[qb] = m * c;
+      grow |= mx[qb] > mref[qb] + kRescaleThreshold;
+    }
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {  // some row of the wave needs a new reference
+#pragma unroll
+      for (int qb = 0; qb < S::kQB; ++qb) {
+        const float mnew = fmaxf(mref[qb], mx[qb]);
+        const float alpha = mnew == -INFINITY ? 1.f : exp2f(mref[qb] - mnew);
+        mref[qb] = mnew;
+        lsum[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < S::kDB; ++db) oacc[db][qb] *= alpha;
+      }
+    }
+
+    u32x4 pb[S::kKB][S::kQB][2];
+#pragma unroll
+    for (int qb = 0; qb < S::kQB; ++qb) {
+      const float mb = mref[qb] == -INFINITY ? 0.f : mref[qb];
+      float rs = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < S::kKB; ++kb)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][qb][8 * t + 2 * e], c, -mb));
+            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][qb][8 * t + 2 * e + 1], c, -mb));
+            pb[kb][qb][t][e] = pack_p<kBf>(p0, p1);
+            rs += p0 + p1;  // float32 sum of the unrounded probabilities (lse needs it)
+          }
+      lsum[qb] += rs;
+    }
+
+    // ---- O^T += V^T P^T.  Element e of lane (half, col) of the V^T operand is
+    // V[32*kb + 16*t + 8*(e/4) + 4*half + e%4][col], matching the key held in
+    // element e of the P operand (accumulator row 8*t + e of the S^T block).
+    const int g = lane >> 4, u = lane & 15;
+#pragma unroll
+    for (int db = 0; db < S::kDB; ++db) {
+#pragma unroll
+      for (int kb = 0; kb < S::kKB; ++kb)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          u32x4 a;
+          if constexpr (Tr::kFp8) {
+            // 8 fp8 keys per lane: rows key(e) for e = u/2 and u/2 + ... via the 8-bit transposing read
+            const int col = 32 * db + 16 * (g & 1) + 8 * (u & 1);  // byte column this lane addresses
+            const int ep = u >> 1;
+            const int row = kb * 32 + 16 * t + 8 * (ep >> 2) + 4 * half + (ep & 3);
+            const u32x2 x = lds_read_tr8(lv, (row * S::kCV + ((col >> 4) ^ swz<S::kCV>(row))) * 16 + (col & 15));
+            const bf16x2 w0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)x[0], 1.0f, false);
+            const bf16x2 w1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)x[0], 1.0f, true);
+            const bf16x2 w2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)x[1], 1.0f, false);
+            const bf16x2 w3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)x[1], 1.0f, true);
+            a = u32x4{__builtin_bit_cast(u32, w0), __builtin_bit_cast(u32, w1), __builtin_bit_cast(u32, w2),
+                      __builtin_bit_cast(u32, w3)};
+          } else {
+            const int col = 32 * db + 16 * (g & 1) + 4 * (u & 3);  // element column this lane addresses
+            const int r0 = kb * 32 + 16 * t + 4 * half + (u >> 2);
+            const int r1 = r0 + 8;
+            const u32x2 lo = lds_read_tr16(lv, (r0 * S::kCV + ((col >> 3) ^ swz<S::kCV>(r0))) * 16 + (col & 7) * 2);
+            const u32x2 hi = lds_read_tr16(lv, (r1 * S::kCV + ((col >> 3) ^ swz<S::kCV>(r1))) * 16 + (col & 7) * 2);
+            a = u32x4{lo[0], lo[1], hi[0], hi[1]};
+          }
+#pragma unroll
+          for (int qb = 0; qb < S::kQB; ++qb) oacc[db][qb] = mfma16(a, pb[kb][qb][t], oacc[db][qb], kBf);
+        }
+    }
+  };
+
+  // ---- main loop: two LDS stages, one barrier per tile
+  issue_tile(0, lds_k0, lds_v0);
+  for (int kt = 0; kt < n_kv; kt += 2) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // tile kt landed for every wave; stage 1 is no longer read
+    if (kt + 1 < n_kv) issue_tile(kt + 1, lds_k1, lds_v1);
+    if (!(CAUSAL && kt * BC > qw0 + QW - 1)) compute(kt, lds_k0, lds_v0);
+    if (kt + 1 < n_kv) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (kt + 2 < n_kv) issue_tile(kt + 2, lds_k0, lds_v0);
+      if (!(CAUSAL && (kt + 1) * BC > qw0 + QW - 1)) compute(kt + 1, lds_k1, lds_v1);
+    }
+  }
+
+  // ---- epilogue: combine the half-wave sums, normalise, store
+#pragma unroll
+  for (int qb = 0; qb < S::kQB; ++qb) {
+    const int qi = qw0 + 32 * qb + l32;
+    const float l_tot = lsum[qb] + __shfl_xor(lsum[qb], 32);
+    const float inv = l_tot > 0.f ? p.o_mul / l_tot : 0.f;
+    if (qi < N) {
+      if (half == 0) p.lse[(size_t)bh * N + qi] = l_tot > 0.f ? (mref[qb] + __log2f(l_tot)) * kLn2 : -INFINITY;
+      char* orow = (char*)p.o + ((size_t)bh * N + qi) * D * 2;
+#pragma unroll
+      for (int db = 0; db < S::kDB; ++db)
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4) {
+          const int col = 32 * db + 8 * a4 + 4 * half;
+          u32x2 w;
+          w[0] = pack_p<kBf>(oacc[db][qb][4 * a4 + 0] * inv, oacc[db][qb][4 * a4 + 1] * inv);
+          w[1] = pack_p<kBf>(oacc[db][qb][4 * a4 + 2] * inv, oacc[db][qb][4 * a4 + 3] * inv);
+          *reinterpret_cast<u32x2*>(orow + col * 2) = w;
+        }
+    }
+  }
+}
+
+namespace {
+
+// ---------------------------------------------------------------- instances
+struct Variant {
+  int qw, nw, bc;
+};
+
+template <class Tr, int D, bool CAUSAL, int QW, int NW, int BC>
+hipError_t launch_one(const FwdParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL((fa_fwd_kernel<Tr, D, CAUSAL, QW, NW, BC>), dim3(p.total_wg), dim3(NW * 64), 0, stream, p);
+  return hipGetLastError();
+}
+
+// Tile shapes compiled for every (dtype, d, causal), as {QW, NW, BC}.
+// FA_TILE=<qw>x<nw>x<bc> selects one of them instead of the default (tile
+// sweeps only; an unknown value falls back to the default).
+constexpr Variant kVariants[] = {{32, 8, 64}, {64, 4, 64}, {32, 4, 64}, {64, 8, 64}};
+constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
+
+int default_variant(Dtype, int, bool) { return 0; }
+
+int selected_variant(Dtype dt, int d, bool causal) {
+  const char* env = getenv("FA_TILE");
+  if (env) {
+    int qw = 0, nw = 0, bc = 0;
+    if (sscanf(env, "%dx%dx%d", &qw, &nw, &bc) == 3)
+      for (int i = 0; i < kNumVariants; ++i)
+        if (kVariants[i].qw == qw && kVariants[i].nw == nw && kVariants[i].bc == bc) return i;
+  }
+  return default_variant(dt, d, causal);
+}
+
+template <class Tr, int D, bool CAUSAL>
+hipError_t dispatch_variant(int v, const FwdParams& p, hipStream_t stream) {
+  switch (v) {
+    case 1: return launch_one<Tr, D, CAUSAL, 64, 4, 64>(p, stream);
+    case 2: return launch_one<Tr, D, CAUSAL, 32, 4, 64>(p, stream);
+    case 3: return launch_one<Tr, D, CAUSAL, 64, 8, 64>(p, stream);
+    default: return launch_one<Tr, D, CAUSAL, 32, 8, 64>(p, stream);
+  }
+}
+
+template <class Tr>
+hipError_t dispatch_dtype(Dtype dt, int d, bool causal, const FwdParams& p, hipStream_t stream) {
+  const int v = selected_variant(dt, d, causal);
+  if (d == 64) return causal ? dispatch_variant<Tr, 64, true>(v, p, stream) : dispatch_variant<Tr, 64, false>(v, p, stream);
+  return causal ? dispatch_variant<Tr, 128, true>(v, p, stream) : dispatch_variant<Tr, 128, false>(v, p, stream);
+}
+
+}  // namespace
+
+int rows_per_workgroup(Dtype dt, int d, bool causal) {
+  const Variant& v = kVariants[selected_variant(dt, d, causal)];
+  return v.qw * v.nw;
+}
+
+hipError_t launch_fwd(Dtype dt, int d, bool causal, const FwdParams& p, hipStream_t stream) {
+  if (d != 64 && d != 128) return hipErrorInvalidValue;
+  switch (dt) {
+    case Dtype::F16: return dispatch_dtype<TrF16>(dt, d, causal, p, stream);
+    case Dtype::BF16: return dispatch_dtype<TrBF16>(dt, d, causal, p, stream);
+    case Dtype::FP8: return dispatch_dtype<TrFP8>(dt, d, causal, p, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace fa

@@ -1,0 +1,140 @@
+"""C ABI of libfa.so without a GPU: symbols, version, error codes.
+
+Only argument-rejection paths are exercised; they return before any HIP call,
+so these run on a machine with no GPU.  No test here passes arguments that
+would launch a kernel.
+"""
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+from io_aware_attention_fwd_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+
+def _header():
+    return open(HEADER).read()
+
+
+def _declared_functions():
+    text = re.sub(r"/\*.*?\*/", "", _header(), flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?(?:int|void|char|float)\s*\**\s*(fa_\w+)\s*\(", text, flags=re.M)))
+
+
+def _codes():
+    return {name: int(val) for name, val in re.findall(r"(FA_(?:OK|ERR_\w+))\s*=\s*(-?\d+)", _header())}
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.library_path()):
+        pytest.fail("libfa.so is not built; run __graft_entry__.build()")
+    return _lib.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    declared = _declared_functions()
+    assert declared == ["fa_fwd", "fa_fwd_fp8", "fa_strerror", "fa_version"]
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.library_path()], capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (fa_\w+)$", out, flags=re.M))
+    for name in declared:
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_version_matches_header(lib):
+    ver = int(re.search(r"#define FA_VERSION (\d+)", _header()).group(1))
+    assert _lib.fa_version() == ver
+
+
+def test_strerror_covers_every_code(lib):
+    codes = _codes()
+    assert codes["FA_OK"] == 0 and len(codes) == 9
+    texts = {_lib.fa_strerror(c) for c in codes.values()}
+    assert len(texts) == len(codes) and "unknown error code" not in texts
+    assert _lib.fa_strerror(12345) == "unknown error code"
+
+
+# Fake, well-aligned, non-overlapping addresses: every call below is rejected
+# before the library touches them.  Should a validation bug ever let one
+# through, the library would launch on these addresses, so the rejection tests
+# only run where no GPU is visible.
+no_gpu = pytest.mark.skipif(__import__("torch").cuda.is_available(),
+                            reason="fake device addresses must never reach a real GPU")
+BASE = 0x7F0000000000
+SPAN = 1 << 36
+
+
+def _args(**kw):
+    a = dict(q=BASE, k=BASE + SPAN, v=BASE + 2 * SPAN, o=BASE + 3 * SPAN, lse=BASE + 4 * SPAN,
+             B=2, H=4, N=1000, d=64, scale=0.125, causal=0, dtype=_lib.FA_DTYPE_F16, stream=None)
+    a.update(kw)
+    return a
+
+
+def _call(**kw):
+    a = _args(**kw)
+    return _lib.fa_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"], a["d"], a["scale"],
+                       a["causal"], a["dtype"], a["stream"])
+
+
+def _call8(descale=(1.0, 1.0, 1.0), **kw):
+    a = _args(**kw)
+    return _lib.fa_fwd_fp8(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"], a["d"], a["scale"],
+                           a["causal"], descale[0], descale[1], descale[2], a["stream"])
+
+
+@pytest.mark.parametrize("case,kw,code", [
+    ("null q", dict(q=None), "FA_ERR_NULL_PTR"),
+    ("null lse", dict(lse=None), "FA_ERR_NULL_PTR"),
+    ("B=0", dict(B=0), "FA_ERR_SHAPE"),
+    ("H<0", dict(H=-3), "FA_ERR_SHAPE"),
+    ("N=0", dict(N=0), "FA_ERR_SHAPE"),
+    ("slice >= 2 GiB", dict(N=(1 << 31) // (64 * 2)), "FA_ERR_SHAPE"),
+    ("too many workgroups", dict(B=1 << 16, H=1 << 14, N=1 << 10), "FA_ERR_SHAPE"),
+    ("d=32", dict(d=32), "FA_ERR_HEADDIM"),
+    ("d=96", dict(d=96), "FA_ERR_HEADDIM"),
+    ("dtype=3", dict(dtype=3), "FA_ERR_DTYPE"),
+    ("dtype=-1", dict(dtype=-1), "FA_ERR_DTYPE"),
+    ("scale nan", dict(scale=math.nan), "FA_ERR_SCALE"),
+    ("scale inf", dict(scale=math.inf), "FA_ERR_SCALE"),
+    ("q misaligned", dict(q=BASE + 8), "FA_ERR_ALIGN"),
+    ("o misaligned", dict(o=BASE + 3 * SPAN + 2), "FA_ERR_ALIGN"),
+    ("lse misaligned", dict(lse=BASE + 4 * SPAN + 2), "FA_ERR_ALIGN"),
+    ("o is q", dict(o=BASE), "FA_ERR_ALIAS"),
+    ("o overlaps v tail", dict(o=BASE + 2 * SPAN + 16 * 1024), "FA_ERR_ALIAS"),
+    ("lse inside k", dict(lse=BASE + SPAN + 4096), "FA_ERR_ALIAS"),
+    ("lse inside o", dict(lse=BASE + 3 * SPAN + 64), "FA_ERR_ALIAS"),
+])
+@no_gpu
+def test_fa_fwd_rejects(lib, case, kw, code):
+    assert _call(**kw) == _codes()[code], case
+
+
+@pytest.mark.parametrize("descale,kw,code", [
+    ((math.nan, 1.0, 1.0), {}, "FA_ERR_SCALE"),
+    ((1.0, math.inf, 1.0), {}, "FA_ERR_SCALE"),
+    ((1.0, 1.0, -math.inf), {}, "FA_ERR_SCALE"),
+    ((1e30, 1e30, 1.0), {}, "FA_ERR_SCALE"),  # folded multiplier overflows float32
+    ((1.0, 1.0, 1.0), dict(d=256), "FA_ERR_HEADDIM"),
+    ((1.0, 1.0, 1.0), dict(k=None), "FA_ERR_NULL_PTR"),
+    ((1.0, 1.0, 1.0), dict(N=(1 << 31) // 64), "FA_ERR_SHAPE"),
+])
+@no_gpu
+def test_fa_fwd_fp8_rejects(lib, descale, kw, code):
+    assert _call8(descale, **kw) == _codes()[code]
+
+
+def test_python_wrapper_rejects_mismatched_shapes():
+    import torch
+    q = torch.zeros(1, 2, 8, 64, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        _lib.fwd(q, torch.zeros(1, 2, 9, 64, dtype=torch.float16), q, 0.1)
+    with pytest.raises(TypeError):
+        _lib.fwd(q.float(), q.float(), q.float(), 0.1)
