@@ -104,6 +104,29 @@ __device__ __forceinline__ u32 pack_p(float lo, float hi) {
   return __builtin_bit_cast(u32, __builtin_convertvector(x, f16x2));
 }
 
+// Combine lane l with lane l ^ 32 (the other half-wave) without touching LDS
+// (an LDS permute would be ordered behind the operand reads in flight).
+// v_permlane32_swap exchanges the upper half-wave of its first operand with
+// the lower half-wave of its second; applied to two copies of x it leaves the
+// lower half-wave's values in every lane of one and the upper half-wave's in
+// every lane of the other, so a symmetric combination of the two gives each
+// lane the pairwise result.  It is written as inline assembly because the
+// compiler's model of the builtin folds that symmetric combination into a
+// single operand.
+__device__ __forceinline__ void swap_halves(u32& a, u32& b) {
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ float halves_max(float x) {
+  u32 a = __builtin_bit_cast(u32, x), b = a;
+  swap_halves(a, b);
+  return fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  u32 a = __builtin_bit_cast(u32, x), b = a;
+  swap_halves(a, b);
+  return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
+}
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, u32 bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, (int)kRsrcWord3);
 }
@@ -140,11 +163,21 @@ __device__ __forceinline__ int xcd_remap(int wg, int total) {
   return xcd < rem ? xcd * (per + 1) + pos : rem * (per + 1) + (xcd - rem) * per + pos;
 }
 
-// XOR swizzle of the 16-byte chunks of LDS row r (chunks per row = CPR).
-template <int CPR>
+// XOR swizzle of the 16-byte chunks of LDS row r, for rows of RB bytes.
+// The LDS has 64 four-byte banks (256 bytes per cycle): a 128-bit read is
+// served 16 lanes per cycle and a 64-bit (transposing) read 32 lanes per
+// cycle.  The patterns below keep both kinds of operand read conflict-free:
+//   * K reads: 16 consecutive rows, one logical chunk each;
+//   * V^T reads: 4 consecutive rows x 4 consecutive chunks (16-bit values) or
+//     rows {r..r+3, r+8..r+11} x 2 chunks (8-bit values).
+// Every pattern depends on r mod 16 only, so row offsets that are multiples
+// of 16 keep the swizzle and fold into immediate address offsets.
+template <int RB>
 __device__ __forceinline__ int swz(int r) {
-  constexpr int kMask = CPR >= 8 ? 7 : CPR - 1;
-  return (r ^ (r >> 3)) & kMask;
+  static_assert(RB == 64 || RB == 128 || RB == 256, "row size");
+  if (RB == 64) return (r >> 2) & 3;
+  if (RB == 128) return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+  return ((r & 3) << 2) | ((r >> 2) & 3);
 }
 
 template <class Tr, int D, int QW, int NW, int BC>
@@ -169,8 +202,9 @@ struct Shape {
 
 // The kernel template has external linkage so that every instantiation's
 // host-side launch stub is emitted.
-template <class Tr, int D, bool CAUSAL, int QW, int NW, int BC>
-__global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(FwdParams p) {
+template <class Tr, int D, bool CAUSAL, int QW, int NW, int BC, bool PP, int WPE>
+__global__ __launch_bounds__(NW * 64, WPE) void fa_fwd_kernel(FwdParams p) {
+  static_assert(!PP || NW == 8, "the ping-pong schedule pairs waves w and w+4 on one SIMD");
   using S = Shape<Tr, D, QW, NW, BC>;
   constexpr bool kBf = Tr::kPvBf16;
   __shared__ __attribute__((aligned(1024))) char lds_k0[S::kSK];
@@ -234,7 +268,7 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(FwdParams p) {
   // ---- direct HBM -> LDS tile loads.  Lane L of a 1 KiB block instruction
   // writes LDS granule 64*blk + L; it fetches the logical chunk that the
   // swizzle places there.
-  auto issue_tile = [&](int kt, char* dk, char* dv) {
+  auto issue_k = [&](int kt, char* dk) __attribute__((always_inline)) {
     const int k0 = kt * BC;
 #pragma unroll
     for (int j = 0; j < (S::kBlkK + NW - 1) / NW; ++j) {
@@ -242,17 +276,20 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(FwdParams p) {
       if (blk < S::kBlkK) {
         const int g = blk * 64 + lane;
         const int r = g / S::kCK, pc = g % S::kCK;
-        const int lc = pc ^ swz<S::kCK>(r);
+        const int lc = pc ^ swz<S::kRK>(r);
         load_lds16(rk, dk + blk * 1024, (k0 + r) * S::kRK + lc * 16);
       }
     }
+  };
+  auto issue_v = [&](int kt, char* dv) __attribute__((always_inline)) {
+    const int k0 = kt * BC;
 #pragma unroll
     for (int j = 0; j < (S::kBlkV + NW - 1) / NW; ++j) {
       const int blk = wave + j * NW;
       if (blk < S::kBlkV) {
         const int g = blk * 64 + lane;
         const int r = g / S::kCV, pc = g % S::kCV;
-        const int lc = pc ^ swz<S::kCV>(r);
+        const int lc = pc ^ swz<S::kRV>(r);
         load_lds16(rv, dv + blk * 1024, (k0 + r) * S::kRV + lc * 16);
       }
     }
@@ -271,33 +308,59 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(FwdParams p) {
   }
   const float c = p.c;
 
-  auto compute = [&](int kt, const char* lk, const char* lv) {
-    const int k0 = kt * BC;
-    // ---- S^T = K Q^T
-    f32x16 sacc[S::kKB][S::kQB];
+  // Scores of the tile between its matrix phase and its softmax phase, and
+  // probabilities between the softmax phase and the next matrix phase.
+  f32x16 sacc[S::kKB][S::kQB];
+  u32x4 pb[S::kKB][S::kQB][2];
+
+  // Operand registers.  All LDS reads of a product are issued before its
+  // first matrix instruction so that their latencies overlap.
+  u32x4 kop16[S::kKB][Tr::kFp8 ? 1 : S::kQSteps];
+  i32x8 kop8[S::kKB][Tr::kFp8 ? S::kQSteps : 1];
+  u32x4 vop16[S::kDB][S::kKB][2];
+  u32x2 vop8[S::kDB][S::kKB][Tr::kFp8 ? 2 : 1];
+
+  // ---- K operands: lane (half, l32) of block kb reads key row 32*kb + l32,
+  // k-group `half` of each instruction step.
+  auto load_k = [&](const char* lk) __attribute__((always_inline)) {
 #pragma unroll
     for (int kb = 0; kb < S::kKB; ++kb) {
-#pragma unroll
-      for (int qb = 0; qb < S::kQB; ++qb) sacc[kb][qb] = f32x16{};
       const int r = kb * 32 + l32;
-      const int sw = swz<S::kCK>(r);
+      const int sw = swz<S::kRK>(r);
 #pragma unroll
       for (int s = 0; s < S::kQSteps; ++s) {
         if constexpr (Tr::kFp8) {
           const u32x4 a0 = lds_read_b128(lk, (r * S::kCK + ((4 * s + 2 * half) ^ sw)) * 16);
           const u32x4 a1 = lds_read_b128(lk, (r * S::kCK + ((4 * s + 2 * half + 1) ^ sw)) * 16);
-          const i32x8 a = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
-                           (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
-#pragma unroll
-          for (int qb = 0; qb < S::kQB; ++qb) sacc[kb][qb] = mfma_fp8(a, q8[qb][s], sacc[kb][qb]);
+          kop8[kb][s] = i32x8{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
+                              (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
         } else {
-          const u32x4 a = lds_read_b128(lk, (r * S::kCK + ((2 * s + half) ^ sw)) * 16);
-#pragma unroll
-          for (int qb = 0; qb < S::kQB; ++qb) sacc[kb][qb] = mfma16(a, q16[qb][s], sacc[kb][qb], kBf);
+          kop16[kb][s] = lds_read_b128(lk, (r * S::kCK + ((2 * s + half) ^ sw)) * 16);
         }
       }
     }
+  };
 
+  // ---- S^T = K Q^T
+  auto mma_qk = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int kb = 0; kb < S::kKB; ++kb) {
+#pragma unroll
+      for (int qb = 0; qb < S::kQB; ++qb) sacc[kb][qb] = f32x16{};
+#pragma unroll
+      for (int s = 0; s < S::kQSteps; ++s)
+#pragma unroll
+        for (int qb = 0; qb < S::kQB; ++qb) {
+          if constexpr (Tr::kFp8)
+            sacc[kb][qb] = mfma_fp8(kop8[kb][s], q8[qb][s], sacc[kb][qb]);
+          else
+            sacc[kb][qb] = mfma16(kop16[kb][s], q16[qb][s], sacc[kb][qb], kBf);
+        }
+    }
+  };
+
+  auto softmax = [&](int kt) __attribute__((always_inline)) {
+    const int k0 = kt * BC;
     // ---- mask keys past N and (causal) keys after the query
     const bool need_mask = (k0 + BC > N) || (CAUSAL && k0 + BC - 1 > qw0);
     if (need_mask) {
@@ -315,18 +378,20 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(FwdParams p) {
       }
     }
 
-    // ---- online softmax with lazy rescaling
+    // ---- online softmax with lazy rescaling.  Reductions use several
+    // independent partial results so that no long dependency chain forms.
     float mx[S::kQB];
     bool grow = false;
 #pragma unroll
     for (int qb = 0; qb < S::kQB; ++qb) {
-      float m = -INFINITY;
+      float part[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
       for (int kb = 0; kb < S::kKB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) m = fmaxf(m, sacc[kb][qb][r]);
-      m = fmaxf(m, __shfl_xor(m, 32));
-      mx[qb] = m * c;
+        for (int r = 0; r < 16; r += 2)
+          part[(kb * 8 + r / 2) & 3] = fmaxf(part[(kb * 8 + r / 2) & 3], fmaxf(sacc[kb][qb][r], sacc[kb][qb][r + 1]));
+      const float m = fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3]));
+      mx[qb] = halves_max(m) * c;
       grow |= mx[qb] > mref[qb] + kRescaleThreshold;
     }
     if (__builtin_amdgcn_ballot_w64(grow) != 0) {  // some row of the wave needs a new reference
@@ -341,11 +406,10 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(FwdParams p) {
       }
     }
 
-    u32x4 pb[S::kKB][S::kQB][2];
 #pragma unroll
     for (int qb = 0; qb < S::kQB; ++qb) {
       const float mb = mref[qb] == -INFINITY ? 0.f : mref[qb];
-      float rs = 0.f;
+      float rs[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < S::kKB; ++kb)
 #pragma unroll
@@ -355,28 +419,51 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(FwdParams p) {
             const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][qb][8 * t + 2 * e], c, -mb));
             const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][qb][8 * t + 2 * e + 1], c, -mb));
             pb[kb][qb][t][e] = pack_p<kBf>(p0, p1);
-            rs += p0 + p1;  // float32 sum of the unrounded probabilities (lse needs it)
+            rs[e] += p0 + p1;  // float32 sums of the unrounded probabilities (lse needs them)
           }
-      lsum[qb] += rs;
+      lsum[qb] += (rs[0] + rs[1]) + (rs[2] + rs[3]);
     }
+  };
 
-    // ---- O^T += V^T P^T.  Element e of lane (half, col) of the V^T operand is
-    // V[32*kb + 16*t + 8*(e/4) + 4*half + e%4][col], matching the key held in
-    // element e of the P operand (accumulator row 8*t + e of the S^T block).
+  // ---- V^T operands.  Element e of lane (half, col) of the V^T operand is
+  // V[32*kb + 16*t + 8*(e/4) + 4*half + e%4][col], matching the key held in
+  // element e of the P operand (accumulator row 8*t + e of the S^T block).
+  auto load_v = [&](const char* lv) __attribute__((always_inline)) {
     const int g = lane >> 4, u = lane & 15;
 #pragma unroll
-    for (int db = 0; db < S::kDB; ++db) {
+    for (int db = 0; db < S::kDB; ++db)
+#pragma unroll
+      for (int kb = 0; kb < S::kKB; ++kb)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          if constexpr (Tr::kFp8) {
+            // 8 keys of one byte column per lane from the 8-bit transposing read
+            const int col = 32 * db + 16 * (g & 1) + 8 * (u & 1);  // byte column this lane addresses
+            const int ep = u >> 1;
+            const int row = kb * 32 + 16 * t + 8 * (ep >> 2) + 4 * half + (ep & 3);
+            vop8[db][kb][t] = lds_read_tr8(lv, (row * S::kCV + ((col >> 4) ^ swz<S::kRV>(row))) * 16 + (col & 15));
+          } else {
+            const int col = 32 * db + 16 * (g & 1) + 4 * (u & 3);  // element column this lane addresses
+            const int r0 = kb * 32 + 16 * t + 4 * half + (u >> 2);
+            const int r1 = r0 + 8;
+            const u32x2 lo = lds_read_tr16(lv, (r0 * S::kCV + ((col >> 3) ^ swz<S::kRV>(r0))) * 16 + (col & 7) * 2);
+            const u32x2 hi = lds_read_tr16(lv, (r1 * S::kCV + ((col >> 3) ^ swz<S::kRV>(r1))) * 16 + (col & 7) * 2);
+            vop16[db][kb][t] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+          }
+        }
+  };
+
+  // ---- O^T += V^T P^T (fp8 values are widened exactly to bfloat16 here)
+  auto mma_pv = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int db = 0; db < S::kDB; ++db)
 #pragma unroll
       for (int kb = 0; kb < S::kKB; ++kb)
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           u32x4 a;
           if constexpr (Tr::kFp8) {
-            // 8 fp8 keys per lane: rows key(e) for e = u/2 and u/2 + ... via the 8-bit transposing read
-            const int col = 32 * db + 16 * (g & 1) + 8 * (u & 1);  // byte column this lane addresses
-            const int ep = u >> 1;
-            const int row = kb * 32 + 16 * t + 8 * (ep >> 2) + 4 * half + (ep & 3);
-            const u32x2 x = lds_read_tr8(lv, (row * S::kCV + ((col >> 4) ^ swz<S::kCV>(row))) * 16 + (col & 15));
+            const u32x2 x = vop8[db][kb][t];
             const bf16x2 w0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)x[0], 1.0f, false);
             const bf16x2 w1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)x[0], 1.0f, true);
             const bf16x2 w2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)x[1], 1.0f, false);
@@ -384,31 +471,113 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(FwdParams p) {
             a = u32x4{__builtin_bit_cast(u32, w0), __builtin_bit_cast(u32, w1), __builtin_bit_cast(u32, w2),
                       __builtin_bit_cast(u32, w3)};
           } else {
-            const int col = 32 * db + 16 * (g & 1) + 4 * (u & 3);  // element column this lane addresses
-            const int r0 = kb * 32 + 16 * t + 4 * half + (u >> 2);
-            const int r1 = r0 + 8;
-            const u32x2 lo = lds_read_tr16(lv, (r0 * S::kCV + ((col >> 3) ^ swz<S::kCV>(r0))) * 16 + (col & 7) * 2);
-            const u32x2 hi = lds_read_tr16(lv, (r1 * S::kCV + ((col >> 3) ^ swz<S::kCV>(r1))) * 16 + (col & 7) * 2);
-            a = u32x4{lo[0], lo[1], hi[0], hi[1]};
+            a = vop16[db][kb][t];
           }
 #pragma unroll
           for (int qb = 0; qb < S::kQB; ++qb) oacc[db][qb] = mfma16(a, pb[kb][qb][t], oacc[db][qb], kBf);
         }
-    }
   };
 
-  // ---- main loop: two LDS stages, one barrier per tile
-  issue_tile(0, lds_k0, lds_v0);
-  for (int kt = 0; kt < n_kv; kt += 2) {
+  // Interleaved forms: each operand is read right before its instruction,
+  // which keeps fewer operand registers live (used where registers are short).
+  auto qk_interleaved = [&](const char* lk) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kb = 0; kb < S::kKB; ++kb) {
+#pragma unroll
+      for (int qb = 0; qb < S::kQB; ++qb) sacc[kb][qb] = f32x16{};
+      const int r = kb * 32 + l32;
+      const int sw = swz<S::kRK>(r);
+#pragma unroll
+      for (int s = 0; s < S::kQSteps; ++s) {
+        if constexpr (Tr::kFp8) {
+          const u32x4 a0 = lds_read_b128(lk, (r * S::kCK + ((4 * s + 2 * half) ^ sw)) * 16);
+          const u32x4 a1 = lds_read_b128(lk, (r * S::kCK + ((4 * s + 2 * half + 1) ^ sw)) * 16);
+          const i32x8 a = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
+                           (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+#pragma unroll
+          for (int qb = 0; qb < S::kQB; ++qb) sacc[kb][qb] = mfma_fp8(a, q8[qb][s], sacc[kb][qb]);
+        } else {
+          const u32x4 a = lds_read_b128(lk, (r * S::kCK + ((2 * s + half) ^ sw)) * 16);
+#pragma unroll
+          for (int qb = 0; qb < S::kQB; ++qb) sacc[kb][qb] = mfma16(a, q16[qb][s], sacc[kb][qb], kBf);
+        }
+      }
+    }
+  };
+  auto pv_interleaved = [&](const char* lv) __attribute__((always_inline)) {
+    load_v(lv);
+    mma_pv();
+  };
+
+  // A wave works on tile kt only if some of its rows can see a key of it.
+  auto active = [&](int kt) __attribute__((always_inline)) { return kt >= 0 && kt < n_kv && !(CAUSAL && kt * BC > qw0 + QW - 1); };
+
+  // ---- main loop: ping-pong between the two waves of each SIMD.
+  // Waves 0-3 (group 0) and 4-7 (group 1) share the four SIMDs pairwise.
+  // Time is cut into phases separated by workgroup barriers; in every phase
+  // one group runs matrix-core work (P V of the previous tile, Q K^T of the
+  // current one) while the other runs the softmax of the tile it has scores
+  // for, so each SIMD overlaps one wave's MFMAs with the other's VALU work.
+  //   phase 2t   : group 0 MFMA(t)            group 1 softmax(t-1)
+  //   phase 2t+1 : group 0 softmax(t)         group 1 MFMA(t)
+  // K(t) lives in stage t%2 for phases 2t..2t+1; V(t) in stage t%2 for phases
+  // 2t+2..2t+3.  Both are issued at phase 2t (K one tile ahead) and waited for
+  // at the end of phase 2t+1.
+  const int group = wave >> 2;
+  auto mfma_phase = [&](int kt, const char* lk, const char* lv_prev) __attribute__((always_inline)) {
+    if (active(kt - 1)) pv_interleaved(lv_prev);
+    if (active(kt)) qk_interleaved(lk);
+  };
+  auto tile_step = [&](int kt, const char* lk, const char* lv_prev, char* k_next, char* v_cur) __attribute__((always_inline)) {
+    if (kt + 1 < n_kv) issue_k(kt + 1, k_next);
+    if (kt < n_kv) issue_v(kt, v_cur);
+    if (group == 0) {
+      mfma_phase(kt, lk, lv_prev);
+    } else if (active(kt - 1)) {
+      softmax(kt - 1);
+    }
+    __syncthreads();
+    if (group == 0) {
+      if (active(kt)) softmax(kt);
+    } else {
+      mfma_phase(kt, lk, lv_prev);
+    }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();  // tile kt landed for every wave; stage 1 is no longer read
-    if (kt + 1 < n_kv) issue_tile(kt + 1, lds_k1, lds_v1);
-    if (!(CAUSAL && kt * BC > qw0 + QW - 1)) compute(kt, lds_k0, lds_v0);
-    if (kt + 1 < n_kv) {
+    __syncthreads();
+  };
+
+  if constexpr (PP) {
+    issue_k(0, lds_k0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    for (int kt = 0; kt <= n_kv; kt += 2) {
+      tile_step(kt, lds_k0, lds_v1, lds_k1, lds_v0);
+      if (kt + 1 <= n_kv) tile_step(kt + 1, lds_k1, lds_v0, lds_k0, lds_v1);
+    }
+  } else {
+    // Plain schedule: every wave runs Q K^T, softmax and P V of a tile in
+    // turn; with several workgroups per CU the waves of different
+    // workgroups interleave matrix-core and vector work on each SIMD.
+    auto plain_step = [&](int kt, const char* kc, const char* vc, char* kn, char* vn) __attribute__((always_inline)) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-      if (kt + 2 < n_kv) issue_tile(kt + 2, lds_k0, lds_v0);
-      if (!(CAUSAL && (kt + 1) * BC > qw0 + QW - 1)) compute(kt + 1, lds_k1, lds_v1);
+      __syncthreads();  // tile kt landed for every wave; the other stage is no longer read
+      if (kt + 1 < n_kv) {
+        issue_k(kt + 1, kn);
+        issue_v(kt + 1, vn);
+      }
+      if (active(kt)) {
+        load_k(kc);
+        mma_qk();
+        load_v(vc);  // in flight during the softmax
+        softmax(kt);
+        mma_pv();
+      }
+    };
+    issue_k(0, lds_k0);
+    issue_v(0, lds_v0);
+    for (int kt = 0; kt < n_kv; kt += 2) {
+      plain_step(kt, lds_k0, lds_v0, lds_k1, lds_v1);
+      if (kt + 1 < n_kv) plain_step(kt + 1, lds_k1, lds_v1, lds_k0, lds_v0);
     }
   }
 
@@ -416,7 +585,7 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(FwdParams p) {
 #pragma unroll
   for (int qb = 0; qb < S::kQB; ++qb) {
     const int qi = qw0 + 32 * qb + l32;
-    const float l_tot = lsum[qb] + __shfl_xor(lsum[qb], 32);
+    const float l_tot = halves_sum(lsum[qb]);
     const float inv = l_tot > 0.f ? p.o_mul / l_tot : 0.f;
     if (qi < N) {
       if (half == 0) p.lse[(size_t)bh * N + qi] = l_tot > 0.f ? (mref[qb] + __log2f(l_tot)) * kLn2 : -INFINITY;
@@ -439,30 +608,36 @@ namespace {
 
 // ---------------------------------------------------------------- instances
 struct Variant {
-  int qw, nw, bc;
+  int qw, nw, bc, pp, wpe;  // rows per wave, waves, keys per tile, ping-pong, min waves per SIMD
 };
 
-template <class Tr, int D, bool CAUSAL, int QW, int NW, int BC>
+template <class Tr, int D, bool CAUSAL, int QW, int NW, int BC, bool PP, int WPE>
 hipError_t launch_one(const FwdParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL((fa_fwd_kernel<Tr, D, CAUSAL, QW, NW, BC>), dim3(p.total_wg), dim3(NW * 64), 0, stream, p);
+  hipLaunchKernelGGL((fa_fwd_kernel<Tr, D, CAUSAL, QW, NW, BC, PP, WPE>), dim3(p.total_wg), dim3(NW * 64), 0, stream,
+                     p);
   return hipGetLastError();
 }
 
-// Tile shapes compiled for every (dtype, d, causal), as {QW, NW, BC}.
-// FA_TILE=<qw>x<nw>x<bc> selects one of them instead of the default (tile
-// sweeps only; an unknown value falls back to the default).
-constexpr Variant kVariants[] = {{32, 8, 64}, {64, 4, 64}, {32, 4, 64}, {64, 8, 64}};
+// Tile shapes compiled for every (dtype, d, causal).  FA_TILE=<qw>x<nw>x<bc>x<pp>x<wpe>
+// selects one of them instead of the default (tile sweeps only; an unknown
+// value falls back to the default).
+constexpr Variant kVariants[] = {
+    {32, 8, 64, 1, 2}, {32, 4, 64, 0, 4}, {32, 8, 64, 0, 4}, {32, 4, 64, 0, 3}, {32, 4, 64, 0, 2}};
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
-int default_variant(Dtype, int, bool) { return 0; }
+// Measured on MI355X: the ping-pong schedule wins at d = 128, the plain
+// schedule with three waves per SIMD at d = 64.
+int default_variant(Dtype, int d, bool) { return d == 128 ? 0 : 3; }
 
 int selected_variant(Dtype dt, int d, bool causal) {
   const char* env = getenv("FA_TILE");
   if (env) {
-    int qw = 0, nw = 0, bc = 0;
-    if (sscanf(env, "%dx%dx%d", &qw, &nw, &bc) == 3)
+    Variant v{};
+    if (sscanf(env, "%dx%dx%dx%dx%d", &v.qw, &v.nw, &v.bc, &v.pp, &v.wpe) == 5)
       for (int i = 0; i < kNumVariants; ++i)
-        if (kVariants[i].qw == qw && kVariants[i].nw == nw && kVariants[i].bc == bc) return i;
+        if (kVariants[i].qw == v.qw && kVariants[i].nw == v.nw && kVariants[i].bc == v.bc &&
+            kVariants[i].pp == v.pp && kVariants[i].wpe == v.wpe)
+          return i;
   }
   return default_variant(dt, d, causal);
 }
@@ -470,10 +645,11 @@ int selected_variant(Dtype dt, int d, bool causal) {
 template <class Tr, int D, bool CAUSAL>
 hipError_t dispatch_variant(int v, const FwdParams& p, hipStream_t stream) {
   switch (v) {
-    case 1: return launch_one<Tr, D, CAUSAL, 64, 4, 64>(p, stream);
-    case 2: return launch_one<Tr, D, CAUSAL, 32, 4, 64>(p, stream);
-    case 3: return launch_one<Tr, D, CAUSAL, 64, 8, 64>(p, stream);
-    default: return launch_one<Tr, D, CAUSAL, 32, 8, 64>(p, stream);
+    case 1: return launch_one<Tr, D, CAUSAL, 32, 4, 64, false, 4>(p, stream);
+    case 2: return launch_one<Tr, D, CAUSAL, 32, 8, 64, false, 4>(p, stream);
+    case 3: return launch_one<Tr, D, CAUSAL, 32, 4, 64, false, 3>(p, stream);
+    case 4: return launch_one<Tr, D, CAUSAL, 32, 4, 64, false, 2>(p, stream);
+    default: return launch_one<Tr, D, CAUSAL, 32, 8, 64, true, 2>(p, stream);
   }
 }
 
