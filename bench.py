@@ -136,7 +136,7 @@ def cpu_baseline(x, causal, scale, budget_s):
                       f"{el:.1f} s; full workload extrapolated to {full_s:.1f} s ({full_s * 1e3:.0f} ms per step)"}
 
 
-def load_traffic(per_launch_flops_ms):
+def load_traffic(_unused=None):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if current."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
@@ -155,6 +155,9 @@ def main(argv=None):
     ap.add_argument("--no-sweep", action="store_true", help="skip the N=512..8192 sweep")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the CPU baseline")
+    ap.add_argument("--shape", default=None,
+                    help="B,H,N,d,dtype,causal to time another shape instead of the headline one "
+                         "(e.g. 2,16,16384,128,bf16,1); the JSON line then names that workload")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="also run one device copy of this many MiB (reference kernel for HBM counters)")
     args = ap.parse_args(argv)
@@ -170,7 +173,11 @@ def main(argv=None):
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
 
-    B, H, N, d, dtype, causal, scale = 8, 32, 1024, 64, "f16", False, 1.0 / 8
+    B, H, N, d, dtype, causal = 8, 32, 1024, 64, "f16", False
+    if args.shape:
+        f = args.shape.split(",")
+        B, H, N, d, dtype, causal = int(f[0]), int(f[1]), int(f[2]), int(f[3]), f[4], f[5] in ("1", "true", "True")
+    scale = 1.0 / math.sqrt(d)
     call, stream, keep = make_call(B, H, N, d, dtype, causal, scale)
     if args.copy_calib_mib:
         n = args.copy_calib_mib * 2 ** 20 // 4
@@ -183,10 +190,10 @@ def main(argv=None):
     fl = flops(B, H, N, d, causal)
     tflops = fl / (ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[dtype]
-    algo_bytes = algorithmic_bytes(B, H, N, d, 2, 2)
+    algo_bytes = algorithmic_bytes(B, H, N, d, 1 if dtype == "fp8" else 2, 2)
 
     sweep = []
-    if not args.no_sweep:
+    if not args.no_sweep and not args.shape:
         for n in (512, 1024, 2048, 4096, 8192):
             c2, st2, keep2 = make_call(B, H, n, d, dtype, False, scale)
             reps = 20 if n >= 4096 else 50
@@ -196,7 +203,7 @@ def main(argv=None):
             del keep2
             torch.cuda.empty_cache()
 
-    traffic = load_traffic(None)
+    traffic = load_traffic(None) if not args.shape else None
     line = {
         "metric": "attention fwd TFLOPS + ms at B=8,H=32,d=64,N=512..8192; % of MFMA peak",
         "value": round(tflops, 2),
@@ -209,8 +216,9 @@ def main(argv=None):
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": dtype,
-        "data": "synthetic: i.i.d. N(0,1) inputs from seed 0, stored as binary16",
-        "config": {"workload": "attention forward B=8 H=32 N=1024 d=64 f16 non-causal scale=1/8",
+        "data": f"synthetic: i.i.d. N(0,1) inputs from seed 0, stored as {dtype}",
+        "config": {"workload": f"attention forward B={B} H={H} N={N} d={d} {dtype} "
+                               f"{'causal' if causal else 'non-causal'} scale=1/sqrt({d})",
                    "B": B, "H": H, "N": N, "d": d, "causal": causal},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(tflops / peak, 4), "traffic": traffic,
