@@ -119,12 +119,25 @@ __device__ __forceinline__ void swap_halves(u32& a, u32& b) {
 __device__ __forceinline__ float halves_max(float x) {
   u32 a = __builtin_bit_cast(u32, x), b = a;
   swap_halves(a, b);
-  return fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
+  return __builtin_elementwise_maximum(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
 }
 __device__ __forceinline__ float halves_sum(float x) {
   u32 a = __builtin_bit_cast(u32, x), b = a;
   swap_halves(a, b);
   return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
+}
+
+// acc + p0 + p1 for the row sum.  binary16 sums the rounded pair with one
+// v_dot2c_f32_f16 (rounding moves the sum by at most 2^-11 relative, well
+// inside the lse bar, and matches the values that enter P V).  bfloat16's
+// 2^-8 rounding would be too coarse for lse, so its sum uses the float32
+// values.
+typedef __fp16 fp16x2 __attribute__((ext_vector_type(2)));
+template <bool BF16>
+__device__ __forceinline__ float sum_pair(u32 packed, float p0, float p1, float acc) {
+  if (BF16) return acc + (p0 + p1);
+  const fp16x2 one = {(__fp16)1.0f, (__fp16)1.0f};
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(fp16x2, packed), one, acc, false);
 }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, u32 bytes) {
@@ -195,6 +208,8 @@ struct Shape {
   static constexpr int kBlkK = kSK / 1024;    // 1 KiB direct-load blocks per K stage
   static constexpr int kBlkV = kSV / 1024;
   static constexpr int kQSteps = Tr::kFp8 ? D / 64 : D / 16;  // QK instructions per 32x32 block
+  static constexpr int kKReads = kKB * kQSteps * (Tr::kFp8 ? 2 : 1);  // 128-bit LDS reads of K per tile
+  static constexpr int kQKMfma = kKB * kQSteps * kQB;                 // Q K^T instructions per tile
   static_assert(kSK % 1024 == 0 && kSV % 1024 == 0, "stage must be whole 1 KiB blocks");
 };
 
@@ -207,6 +222,9 @@ __global__ __launch_bounds__(NW * 64, WPE) void fa_fwd_kernel(FwdParams p) {
   static_assert(!PP || NW == 8, "the ping-pong schedule pairs waves w and w+4 on one SIMD");
   using S = Shape<Tr, D, QW, NW, BC>;
   constexpr bool kBf = Tr::kPvBf16;
+  // Two LDS stages.  Separate arrays let the compiler tell the
+  // direct-to-LDS loads of one stage from the reads of the other (with one
+  // array and computed offsets it waits for every load before any read).
   __shared__ __attribute__((aligned(1024))) char lds_k0[S::kSK];
   __shared__ __attribute__((aligned(1024))) char lds_k1[S::kSK];
   __shared__ __attribute__((aligned(1024))) char lds_v0[S::kSV];
@@ -384,13 +402,15 @@ __global__ __launch_bounds__(NW * 64, WPE) void fa_fwd_kernel(FwdParams p) {
     bool grow = false;
 #pragma unroll
     for (int qb = 0; qb < S::kQB; ++qb) {
-      float part[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+      // IEEE maximum (v_maximum3_f32): no NaN quieting of the inputs needed
+      float part[2] = {-INFINITY, -INFINITY};
 #pragma unroll
       for (int kb = 0; kb < S::kKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; r += 2)
-          part[(kb * 8 + r / 2) & 3] = fmaxf(part[(kb * 8 + r / 2) & 3], fmaxf(sacc[kb][qb][r], sacc[kb][qb][r + 1]));
-      const float m = fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3]));
+          part[r / 2 & 1] = __builtin_elementwise_maximum(
+              part[r / 2 & 1], __builtin_elementwise_maximum(sacc[kb][qb][r], sacc[kb][qb][r + 1]));
+      const float m = __builtin_elementwise_maximum(part[0], part[1]);
       mx[qb] = halves_max(m) * c;
       grow |= mx[qb] > mref[qb] + kRescaleThreshold;
     }
@@ -418,8 +438,9 @@ __global__ __launch_bounds__(NW * 64, WPE) void fa_fwd_kernel(FwdParams p) {
           for (int e = 0; e < 4; ++e) {
             const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][qb][8 * t + 2 * e], c, -mb));
             const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][qb][8 * t + 2 * e + 1], c, -mb));
-            pb[kb][qb][t][e] = pack_p<kBf>(p0, p1);
-            rs[e] += p0 + p1;  // float32 sums of the unrounded probabilities (lse needs them)
+            const u32 w = pack_p<kBf>(p0, p1);
+            pb[kb][qb][t][e] = w;
+            rs[e] = sum_pair<kBf>(w, p0, p1, rs[e]);
           }
       lsum[qb] += (rs[0] + rs[1]) + (rs[2] + rs[3]);
     }
@@ -568,6 +589,10 @@ __global__ __launch_bounds__(NW * 64, WPE) void fa_fwd_kernel(FwdParams p) {
       if (active(kt)) {
         load_k(kc);
         mma_qk();
+        // All K operand reads go out before the first Q K^T instruction.
+        __builtin_amdgcn_sched_group_barrier(0x100, S::kKReads, 0);  // DS reads
+        __builtin_amdgcn_sched_group_barrier(0x008, S::kQKMfma, 0);  // matrix instructions
+        __builtin_amdgcn_sched_barrier(0);
         load_v(vc);  // in flight during the softmax
         softmax(kt);
         mma_pv();
@@ -621,13 +646,12 @@ hipError_t launch_one(const FwdParams& p, hipStream_t stream) {
 // Tile shapes compiled for every (dtype, d, causal).  FA_TILE=<qw>x<nw>x<bc>x<pp>x<wpe>
 // selects one of them instead of the default (tile sweeps only; an unknown
 // value falls back to the default).
-constexpr Variant kVariants[] = {
-    {32, 8, 64, 1, 2}, {32, 4, 64, 0, 4}, {32, 8, 64, 0, 4}, {32, 4, 64, 0, 3}, {32, 4, 64, 0, 2}};
+constexpr Variant kVariants[] = {{32, 8, 64, 1, 2}, {32, 4, 64, 0, 4}, {32, 4, 64, 0, 3}, {32, 4, 64, 0, 2}};
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
 // Measured on MI355X: the ping-pong schedule wins at d = 128, the plain
 // schedule with three waves per SIMD at d = 64.
-int default_variant(Dtype, int d, bool) { return d == 128 ? 0 : 3; }
+int default_variant(Dtype, int d, bool) { return d == 128 ? 0 : 2; }
 
 int selected_variant(Dtype dt, int d, bool causal) {
   const char* env = getenv("FA_TILE");
@@ -646,9 +670,8 @@ template <class Tr, int D, bool CAUSAL>
 hipError_t dispatch_variant(int v, const FwdParams& p, hipStream_t stream) {
   switch (v) {
     case 1: return launch_one<Tr, D, CAUSAL, 32, 4, 64, false, 4>(p, stream);
-    case 2: return launch_one<Tr, D, CAUSAL, 32, 8, 64, false, 4>(p, stream);
-    case 3: return launch_one<Tr, D, CAUSAL, 32, 4, 64, false, 3>(p, stream);
-    case 4: return launch_one<Tr, D, CAUSAL, 32, 4, 64, false, 2>(p, stream);
+    case 2: return launch_one<Tr, D, CAUSAL, 32, 4, 64, false, 3>(p, stream);
+    case 3: return launch_one<Tr, D, CAUSAL, 32, 4, 64, false, 2>(p, stream);
     default: return launch_one<Tr, D, CAUSAL, 32, 8, 64, true, 2>(p, stream);
   }
 }
