@@ -32,7 +32,7 @@ int forward(const void* q, const void* k, const void* v, void* o, float* lse, in
   if (d != 64 && d != 128) return FA_ERR_HEADDIM;
   if (!isfinite(scale) || !isfinite(q_descale) || !isfinite(k_descale) || !isfinite(v_descale)) return FA_ERR_SCALE;
   const int eb = elem_bytes(dt);
-  const int br = fa::rows_per_workgroup(dt, d, causal != 0);
+  const int br = fa::rows_per_workgroup(dt, d, causal != 0, N);
   // One (batch, head) slice, plus the padding rows of its last tile, must be
   // addressable with 32-bit byte offsets (the kernels use buffer loads).
   const int64_t slice_bytes = (int64_t)(N + br) * d * eb;

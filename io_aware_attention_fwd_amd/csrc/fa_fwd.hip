@@ -210,6 +210,8 @@ struct Shape {
   static constexpr int kQSteps = Tr::kFp8 ? D / 64 : D / 16;  // QK instructions per 32x32 block
   static constexpr int kKReads = kKB * kQSteps * (Tr::kFp8 ? 2 : 1);  // 128-bit LDS reads of K per tile
   static constexpr int kQKMfma = kKB * kQSteps * kQB;                 // Q K^T instructions per tile
+  static constexpr int kExpVALU = kKB * kQB * 16 * 3;                   // approx. vector instructions of exp_tile
+  static constexpr int kVReads = kDB * kKB * 2 * (Tr::kFp8 ? 1 : 2);    // transposing LDS reads of V per tile
   static_assert(kSK % 1024 == 0 && kSV % 1024 == 0, "stage must be whole 1 KiB blocks");
 };
 
@@ -217,8 +219,12 @@ struct Shape {
 
 // The kernel template has external linkage so that every instantiation's
 // host-side launch stub is emitted.
-template <class Tr, int D, bool CAUSAL, int QW, int NW, int BC, bool PP, int WPE>
+// SCHED: 0 = plain (every wave runs Q K^T, softmax, P V of a tile in turn),
+//        1 = ping-pong between wave groups, 2 = software pipeline inside each
+//        wave (Q K^T of the next tile interleaved with the softmax of this one).
+template <class Tr, int D, bool CAUSAL, int QW, int NW, int BC, int SCHED, int WPE>
 __global__ __launch_bounds__(NW * 64, WPE) void fa_fwd_kernel(FwdParams p) {
+  constexpr bool PP = SCHED == 1;
   static_assert(!PP || NW == 8, "the ping-pong schedule pairs waves w and w+4 on one SIMD");
   using S = Shape<Tr, D, QW, NW, BC>;
   constexpr bool kBf = Tr::kPvBf16;
@@ -359,27 +365,30 @@ __global__ __launch_bounds__(NW * 64, WPE) void fa_fwd_kernel(FwdParams p) {
     }
   };
 
-  // ---- S^T = K Q^T
-  auto mma_qk = [&]() __attribute__((always_inline)) {
+  // ---- S^T = K Q^T into `dst`
+  auto mma_qk_into = [&](f32x16 (&dst)[S::kKB][S::kQB]) __attribute__((always_inline)) {
 #pragma unroll
     for (int kb = 0; kb < S::kKB; ++kb) {
 #pragma unroll
-      for (int qb = 0; qb < S::kQB; ++qb) sacc[kb][qb] = f32x16{};
+      for (int qb = 0; qb < S::kQB; ++qb) dst[kb][qb] = f32x16{};
 #pragma unroll
       for (int s = 0; s < S::kQSteps; ++s)
 #pragma unroll
         for (int qb = 0; qb < S::kQB; ++qb) {
           if constexpr (Tr::kFp8)
-            sacc[kb][qb] = mfma_fp8(kop8[kb][s], q8[qb][s], sacc[kb][qb]);
+            dst[kb][qb] = mfma_fp8(kop8[kb][s], q8[qb][s], dst[kb][qb]);
           else
-            sacc[kb][qb] = mfma16(kop16[kb][s], q16[qb][s], sacc[kb][qb], kBf);
+            dst[kb][qb] = mfma16(kop16[kb][s], q16[qb][s], dst[kb][qb], kBf);
         }
     }
   };
+  auto mma_qk = [&]() __attribute__((always_inline)) { mma_qk_into(sacc); };
 
-  auto softmax = [&](int kt) __attribute__((always_inline)) {
+  using SArr = f32x16[S::kKB][S::kQB];
+
+  // ---- mask keys past N and (causal) keys after the query
+  auto mask_tile = [&](int kt, SArr& sc) __attribute__((always_inline)) {
     const int k0 = kt * BC;
-    // ---- mask keys past N and (causal) keys after the query
     const bool need_mask = (k0 + BC > N) || (CAUSAL && k0 + BC - 1 > qw0);
     if (need_mask) {
 #pragma unroll
@@ -391,13 +400,16 @@ __global__ __launch_bounds__(NW * 64, WPE) void fa_fwd_kernel(FwdParams p) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-            if (key > lim) sacc[kb][qb][r] = -INFINITY;
+            if (key > lim) sc[kb][qb][r] = -INFINITY;
           }
       }
     }
+  };
 
-    // ---- online softmax with lazy rescaling.  Reductions use several
-    // independent partial results so that no long dependency chain forms.
+  // ---- online softmax with lazy rescaling: row maxima, then (rarely) a new
+  // reference maximum with O and l rescaled.  Reductions use independent
+  // partial results so that no long dependency chain forms.
+  auto max_rescale = [&](SArr& sc) __attribute__((always_inline)) {
     float mx[S::kQB];
     bool grow = false;
 #pragma unroll
@@ -409,7 +421,7 @@ __global__ __launch_bounds__(NW * 64, WPE) void fa_fwd_kernel(FwdParams p) {
 #pragma unroll
         for (int r = 0; r < 16; r += 2)
           part[r / 2 & 1] = __builtin_elementwise_maximum(
-              part[r / 2 & 1], __builtin_elementwise_maximum(sacc[kb][qb][r], sacc[kb][qb][r + 1]));
+              part[r / 2 & 1], __builtin_elementwise_maximum(sc[kb][qb][r], sc[kb][qb][r + 1]));
       const float m = __builtin_elementwise_maximum(part[0], part[1]);
       mx[qb] = halves_max(m) * c;
       grow |= mx[qb] > mref[qb] + kRescaleThreshold;
@@ -425,7 +437,10 @@ __global__ __launch_bounds__(NW * 64, WPE) void fa_fwd_kernel(FwdParams p) {
         for (int db = 0; db < S::kDB; ++db) oacc[db][qb] *= alpha;
       }
     }
+  };
 
+  // ---- probabilities P = exp2(S*c - m) as 16-bit pairs, row sums
+  auto exp_tile = [&](SArr& sc) __attribute__((always_inline)) {
 #pragma unroll
     for (int qb = 0; qb < S::kQB; ++qb) {
       const float mb = mref[qb] == -INFINITY ? 0.f : mref[qb];
@@ -436,14 +451,20 @@ __global__ __launch_bounds__(NW * 64, WPE) void fa_fwd_kernel(FwdParams p) {
         for (int t = 0; t < 2; ++t)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][qb][8 * t + 2 * e], c, -mb));
-            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][qb][8 * t + 2 * e + 1], c, -mb));
+            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][qb][8 * t + 2 * e], c, -mb));
+            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][qb][8 * t + 2 * e + 1], c, -mb));
             const u32 w = pack_p<kBf>(p0, p1);
             pb[kb][qb][t][e] = w;
             rs[e] = sum_pair<kBf>(w, p0, p1, rs[e]);
           }
       lsum[qb] += (rs[0] + rs[1]) + (rs[2] + rs[3]);
     }
+  };
+
+  auto softmax = [&](int kt) __attribute__((always_inline)) {
+    mask_tile(kt, sacc);
+    max_rescale(sacc);
+    exp_tile(sacc);
   };
 
   // ---- V^T operands.  Element e of lane (half, col) of the V^T operand is
@@ -567,13 +588,59 @@ __global__ __launch_bounds__(NW * 64, WPE) void fa_fwd_kernel(FwdParams p) {
     __syncthreads();
   };
 
-  if constexpr (PP) {
+  if constexpr (SCHED == 1) {
     issue_k(0, lds_k0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     for (int kt = 0; kt <= n_kv; kt += 2) {
       tile_step(kt, lds_k0, lds_v1, lds_k1, lds_v0);
       if (kt + 1 <= n_kv) tile_step(kt + 1, lds_k1, lds_v0, lds_k0, lds_v1);
+    }
+  } else if constexpr (SCHED == 2) {
+    // Software pipeline inside each wave: while the softmax of tile t runs on
+    // the vector units, Q K^T of tile t+1 runs on the matrix cores; the two
+    // are interleaved in one instruction stream.  K(t) sits in stage t%2 for
+    // steps t-1 and t, V(t) in stage t%2 for step t; both are issued one step
+    // ahead.
+    f32x16 sacc2[S::kKB][S::kQB];
+    auto pl_step = [&](int kt, SArr& s_cur, SArr& s_next, const char* k_next, const char* v_cur, char* k_dst,
+                       char* v_dst) __attribute__((always_inline)) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();  // K(kt+1) and V(kt) landed; the stages written below are no longer read
+      if (kt + 2 < n_kv) issue_k(kt + 2, k_dst);
+      if (kt + 1 < n_kv) issue_v(kt + 1, v_dst);
+      // No per-wave skipping here: a wave whose rows all precede tile kt
+      // sees only masked scores (P = 0, nothing changes), and Q K^T of a
+      // tile past the end reads a stale stage whose result is never used.
+      // Keeping the step branch-free keeps the softmax and the matrix
+      // instructions in one basic block, where they can be interleaved.
+      load_k(k_next);
+      mask_tile(kt, s_cur);
+      max_rescale(s_cur);
+      load_v(v_cur);
+      exp_tile(s_cur);
+      mma_qk_into(s_next);
+      // V operand reads first, then one matrix instruction and a slice of
+      // the vector work, repeated
+      __builtin_amdgcn_sched_group_barrier(0x100, S::kVReads, 0);
+#pragma unroll
+      for (int i = 0; i < S::kQKMfma; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, S::kExpVALU / S::kQKMfma, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      mma_pv();
+    };
+    issue_k(0, lds_k0);
+    issue_v(0, lds_v0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (n_kv > 1) issue_k(1, lds_k1);
+    load_k(lds_k0);
+    mma_qk_into(sacc);
+    for (int kt = 0; kt < n_kv; kt += 2) {
+      pl_step(kt, sacc, sacc2, lds_k1, lds_v0, lds_k0, lds_v1);
+      if (kt + 1 < n_kv) pl_step(kt + 1, sacc2, sacc, lds_k0, lds_v1, lds_k1, lds_v0);
     }
   } else {
     // Plain schedule: every wave runs Q K^T, softmax and P V of a tile in
@@ -633,60 +700,68 @@ namespace {
 
 // ---------------------------------------------------------------- instances
 struct Variant {
-  int qw, nw, bc, pp, wpe;  // rows per wave, waves, keys per tile, ping-pong, min waves per SIMD
+  int qw, nw, bc, sched, wpe;  // rows per wave, waves, keys per tile, schedule, min waves per SIMD
 };
 
-template <class Tr, int D, bool CAUSAL, int QW, int NW, int BC, bool PP, int WPE>
+template <class Tr, int D, bool CAUSAL, int QW, int NW, int BC, int SCHED, int WPE>
 hipError_t launch_one(const FwdParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL((fa_fwd_kernel<Tr, D, CAUSAL, QW, NW, BC, PP, WPE>), dim3(p.total_wg), dim3(NW * 64), 0, stream,
-                     p);
+  hipLaunchKernelGGL((fa_fwd_kernel<Tr, D, CAUSAL, QW, NW, BC, SCHED, WPE>), dim3(p.total_wg), dim3(NW * 64), 0,
+                     stream, p);
   return hipGetLastError();
 }
 
-// Tile shapes compiled for every (dtype, d, causal).  FA_TILE=<qw>x<nw>x<bc>x<pp>x<wpe>
+// Tile shapes compiled for every (dtype, d, causal).  FA_TILE=<qw>x<nw>x<bc>x<sched>x<wpe>
 // selects one of them instead of the default (tile sweeps only; an unknown
 // value falls back to the default).
-constexpr Variant kVariants[] = {{32, 8, 64, 1, 2}, {32, 4, 64, 0, 4}, {32, 4, 64, 0, 3}, {32, 4, 64, 0, 2}};
+constexpr Variant kVariants[] = {{32, 8, 64, 1, 2}, {32, 4, 64, 0, 4}, {32, 4, 64, 0, 3}, {32, 4, 64, 0, 2},
+                                 {32, 4, 64, 2, 2}, {64, 4, 64, 0, 2}};
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
-// Measured on MI355X: the ping-pong schedule wins at d = 128, the plain
-// schedule with three waves per SIMD at d = 64.
-int default_variant(Dtype, int d, bool) { return d == 128 ? 0 : 2; }
+// Measured on MI355X (A/B in one process): the ping-pong schedule wins at
+// d = 128; at d = 64 the plain schedule, with 64 rows per wave for long
+// non-causal sequences and 32 rows per wave at three waves per SIMD otherwise.
+int default_variant(Dtype dt, int d, bool causal, int N) {
+  if (d == 128) return dt == Dtype::FP8 ? 3 : 0;  // plain at two waves per SIMD for fp8, else ping-pong
+  if (!causal && N >= 2048) return 5;     // 64 rows per wave: half the LDS operand traffic per FLOP
+  return 2;                               // plain, three waves per SIMD
+}
 
-int selected_variant(Dtype dt, int d, bool causal) {
+int selected_variant(Dtype dt, int d, bool causal, int N) {
   const char* env = getenv("FA_TILE");
   if (env) {
     Variant v{};
-    if (sscanf(env, "%dx%dx%dx%dx%d", &v.qw, &v.nw, &v.bc, &v.pp, &v.wpe) == 5)
+    if (sscanf(env, "%dx%dx%dx%dx%d", &v.qw, &v.nw, &v.bc, &v.sched, &v.wpe) == 5)
       for (int i = 0; i < kNumVariants; ++i)
         if (kVariants[i].qw == v.qw && kVariants[i].nw == v.nw && kVariants[i].bc == v.bc &&
-            kVariants[i].pp == v.pp && kVariants[i].wpe == v.wpe)
+            kVariants[i].sched == v.sched && kVariants[i].wpe == v.wpe)
           return i;
   }
-  return default_variant(dt, d, causal);
+  return default_variant(dt, d, causal, N);
 }
 
 template <class Tr, int D, bool CAUSAL>
 hipError_t dispatch_variant(int v, const FwdParams& p, hipStream_t stream) {
   switch (v) {
-    case 1: return launch_one<Tr, D, CAUSAL, 32, 4, 64, false, 4>(p, stream);
-    case 2: return launch_one<Tr, D, CAUSAL, 32, 4, 64, false, 3>(p, stream);
-    case 3: return launch_one<Tr, D, CAUSAL, 32, 4, 64, false, 2>(p, stream);
-    default: return launch_one<Tr, D, CAUSAL, 32, 8, 64, true, 2>(p, stream);
+    case 1: return launch_one<Tr, D, CAUSAL, 32, 4, 64, 0, 4>(p, stream);
+    case 2: return launch_one<Tr, D, CAUSAL, 32, 4, 64, 0, 3>(p, stream);
+    case 3: return launch_one<Tr, D, CAUSAL, 32, 4, 64, 0, 2>(p, stream);
+    case 4: return launch_one<Tr, D, CAUSAL, 32, 4, 64, 2, 2>(p, stream);
+    case 5: return launch_one<Tr, D, CAUSAL, 64, 4, 64, 0, 2>(p, stream);
+    default: return launch_one<Tr, D, CAUSAL, 32, 8, 64, 1, 2>(p, stream);
   }
 }
 
 template <class Tr>
 hipError_t dispatch_dtype(Dtype dt, int d, bool causal, const FwdParams& p, hipStream_t stream) {
-  const int v = selected_variant(dt, d, causal);
+  const int v = selected_variant(dt, d, causal, p.N);
   if (d == 64) return causal ? dispatch_variant<Tr, 64, true>(v, p, stream) : dispatch_variant<Tr, 64, false>(v, p, stream);
   return causal ? dispatch_variant<Tr, 128, true>(v, p, stream) : dispatch_variant<Tr, 128, false>(v, p, stream);
 }
 
 }  // namespace
 
-int rows_per_workgroup(Dtype dt, int d, bool causal) {
-  const Variant& v = kVariants[selected_variant(dt, d, causal)];
+int rows_per_workgroup(Dtype dt, int d, bool causal, int N) {
+  const Variant& v = kVariants[selected_variant(dt, d, causal, N)];
   return v.qw * v.nw;
 }
 

@@ -25,8 +25,8 @@ struct FwdParams {
 
 enum class Dtype { F16 = 0, BF16 = 1, FP8 = 2 };
 
-// Rows of Q one workgroup owns for a given instance (used to size the grid).
-int rows_per_workgroup(Dtype dt, int d, bool causal);
+// Rows of Q one workgroup owns for the instance chosen for this call (sizes the grid).
+int rows_per_workgroup(Dtype dt, int d, bool causal, int N);
 
 // Enqueue one forward pass; returns hipSuccess or the launch error.
 hipError_t launch_fwd(Dtype dt, int d, bool causal, const FwdParams& p, hipStream_t stream);
