@@ -10,8 +10,10 @@ region; K steps are timed with HIP events on the stream the kernel runs on,
 between two device synchronisations.
 
 Throughput is 4*B*H*N^2*d FLOP per step (halved for causal) / time.  The line
-also carries the sequence-length sweep N = 512..8192 at B=8, H=32, d=64 (the
-shape of the benchmark page's forward-time tables), the fraction of the dense
+also carries per-call median / min / p90 times, the sequence-length sweep
+N = 512..8192 at B=8, H=32, d=64 (the shape of the benchmark page's
+forward-time tables) plus d=128 and causal points at N >= 4096, the shader and
+memory clock levels in use under load, the fraction of the dense
 fp16 matrix-core peak, HBM traffic from committed rocprofv3 counters when they
 were taken on the current kernel source, and the CPU oracle timed on a bounded
 sample of the same workload.
@@ -69,12 +71,66 @@ def time_calls(fn, warmup, steps, stream):
     return start.elapsed_time(end) / steps  # ms per call
 
 
-def make_call(B, H, N, d, dtype, causal, scale, seed=0):
+def time_each(fn, warmup, steps, stream):
+    """Per-call durations (ms) from an event pair around every call."""
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in ev:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in ev]
+
+
+def summarize(ms_list, fl, peak):
+    ms = sorted(ms_list)
+    med = float(np.median(ms))
+    p90 = float(np.percentile(ms, 90))
+    t = fl / (med * 1e-3) / 1e12
+    return {"ms_median": round(med, 4), "ms_min": round(ms[0], 4), "ms_p90": round(p90, 4),
+            "tflops": round(t, 1), "frac_of_peak": round(t / peak, 4)}
+
+
+def gpu_clock_state(busy_fn=None):
+    """Shader and memory clock levels from the amdgpu sysfs tables (the source rocm-smi reads),
+    sampled while ``busy_fn`` keeps the GPU loaded, so the level in use under load is the one marked."""
+    import glob
+
+    paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+    if not paths:
+        return None
+    if busy_fn is not None:
+        busy_fn()
+        time.sleep(0.05)
+    out = {}
+    for p in paths:
+        dev = p.split("/")[4]
+        st = {}
+        for name in ("pp_dpm_sclk", "pp_dpm_mclk"):
+            try:
+                with open(os.path.join(os.path.dirname(p), name)) as f:
+                    lines = f.read().split("\n")
+                cur = [l for l in lines if l.rstrip().endswith("*")]
+                st[name[7:]] = cur[0].split(":", 1)[1].strip(" *") if cur else None
+                st[name[7:] + "_levels"] = [l.split(":", 1)[1].strip(" *") for l in lines if ":" in l]
+            except OSError:
+                st[name[7:]] = None
+        out[dev] = st
+    return out
+
+
+def make_call(B, H, N, d, dtype, causal, scale, seed=0, x=None):
     import torch
 
     from io_aware_attention_fwd_amd import _lib, gen
 
-    x = gen.make(B, H, N, d, dtype, seed=seed)
+    if x is None:
+        x = gen.make(B, H, N, d, dtype, seed=seed)
     tdt = {"f16": torch.float16, "bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn}[dtype]
 
     def dev(a):
@@ -188,20 +244,42 @@ def main(argv=None):
         del a, b
     ms = time_calls(call, args.warmup, args.steps, stream)
     fl = flops(B, H, N, d, causal)
-    tflops = fl / (ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[dtype]
+    per_call = summarize(time_each(call, 2, min(args.steps, 50), stream), fl, peak)
+    tflops = fl / (ms * 1e-3) / 1e12
     algo_bytes = algorithmic_bytes(B, H, N, d, 1 if dtype == "fp8" else 2, 2)
 
     sweep = []
+    clocks = None
     if not args.no_sweep and not args.shape:
-        for n in (512, 1024, 2048, 4096, 8192):
-            c2, st2, keep2 = make_call(B, H, n, d, dtype, False, scale)
+        # the benchmark page's forward-time tables: B=8, H=32, d=64, N=512..8192, no mask
+        points = [(n, 64, dtype, False) for n in (512, 1024, 2048, 4096, 8192)]
+        # the >=4096 head-dimension 64/128 cases, also causal and bfloat16
+        points += [(4096, 64, "bf16", True), (8192, 64, "bf16", True), (4096, 128, "f16", False),
+                   (8192, 128, "bf16", False), (8192, 128, "bf16", True)]
+        inputs = {}
+        for n, dd, dt, cz in points:
+            if (n, dd, dt) not in inputs:  # causal and non-causal points share one input draw
+                inputs = {(n, dd, dt): None}
+            c2, st2, keep2 = make_call(B, H, n, dd, dt, cz, 1.0 / math.sqrt(dd), x=inputs[(n, dd, dt)])
+            inputs[(n, dd, dt)] = keep2[0]
             reps = 20 if n >= 4096 else 50
-            m2 = time_calls(c2, 5, reps, st2)
-            t2 = flops(B, H, n, d, False) / (m2 * 1e-3) / 1e12
-            sweep.append({"N": n, "ms": round(m2, 4), "tflops": round(t2, 1), "frac_of_peak": round(t2 / peak, 4)})
+            r = summarize(time_each(c2, 5, reps, st2), flops(B, H, n, dd, cz), PEAK_TFLOPS[dt])
+            sweep.append({"N": n, "d": dd, "dtype": dt, "causal": cz, **r})
+            if clocks is None and n == 8192:
+                def busy(c=c2):
+                    for _ in range(30):
+                        c()
+                clocks = gpu_clock_state(busy)
+                torch.cuda.synchronize()
             del keep2
             torch.cuda.empty_cache()
+    if clocks is None:
+        def busy():
+            for _ in range(max(1, int(50e-3 / max(ms * 1e-3, 1e-6)))):
+                call()
+        clocks = gpu_clock_state(busy)
+        torch.cuda.synchronize()
 
     traffic = load_traffic(None) if not args.shape else None
     line = {
@@ -212,6 +290,7 @@ def main(argv=None):
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 5),
+        "per_call": per_call,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -225,6 +304,9 @@ def main(argv=None):
                      "algorithmic_bytes_per_launch": algo_bytes,
                      "algorithmic_hbm_gbs": round(algo_bytes / (ms * 1e-3) / 1e9, 1)},
         "sweep": sweep,
+        "timing": "HIP events on the kernel's stream; value = K back-to-back calls / elapsed; per_call and "
+                  "sweep = one event pair per call (median, min, p90); no cache flush between calls",
+        "gpu_clocks_under_load": clocks,
     }
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(keep[0], causal, scale, args.cpu_budget)

@@ -176,22 +176,33 @@ __device__ __forceinline__ int xcd_remap(int wg, int total) {
   return xcd < rem ? xcd * (per + 1) + pos : rem * (per + 1) + (xcd - rem) * per + pos;
 }
 
-// XOR swizzle of the 16-byte chunks of LDS row r, for rows of RB bytes.
-// The LDS has 64 four-byte banks (256 bytes per cycle): a 128-bit read is
-// served 16 lanes per cycle and a 64-bit (transposing) read 32 lanes per
-// cycle.  The patterns below keep both kinds of operand read conflict-free:
-//   * K reads: 16 consecutive rows, one logical chunk each;
-//   * V^T reads: 4 consecutive rows x 4 consecutive chunks (16-bit values) or
-//     rows {r..r+3, r+8..r+11} x 2 chunks (8-bit values).
-// Every pattern depends on r mod 16 only, so row offsets that are multiples
-// of 16 keep the swizzle and fold into immediate address offsets.
-template <int RB>
-__device__ __forceinline__ int swz(int r) {
+// LDS tile layouts.  The LDS has 64 four-byte banks (256 bytes per cycle): a
+// 128-bit read is served 16 lanes per cycle and a 64-bit (transposing) read
+// 32 lanes per cycle.  Rows are padded rather than swizzled, so that every
+// operand read of a tile is one per-lane base address plus a compile-time
+// offset (no address arithmetic, and no address registers, per read):
+//   * K rows (read 16 consecutive rows x one 16-byte chunk at a time) are
+//     followed by one 16-byte pad granule, which staggers consecutive rows
+//     by 4 banks (row bytes + 16 is 4 mod 64 words for every row size here).
+//   * V rows are read by the transposing reads as 4 consecutive rows x 64
+//     contiguous bytes (16-bit values) or rows {r..r+3, r+8..r+11} x 32
+//     contiguous bytes (8-bit values); pads after every 1, 2 or 8 rows give
+//     each of those rows its own bank range.  The byte offset of row r is
+//     RB*r + PA*(r >> SA) + PB*(r >> SB); groups of 2^SG rows repeat the same
+//     pattern, and every read's 16-row block offset is a multiple of a group.
+template <int RB, bool FP8>
+struct VLayout {
   static_assert(RB == 64 || RB == 128 || RB == 256, "row size");
-  if (RB == 64) return (r >> 2) & 3;
-  if (RB == 128) return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
-  return ((r & 3) << 2) | ((r >> 2) & 3);
-}
+  static constexpr int PA = FP8 ? 32 : 64;
+  static constexpr int SA = FP8 ? (RB == 64 ? 3 : 1) : (RB == 256 ? 0 : 1);
+  static constexpr int PB = FP8 && RB == 128 ? 64 : 0;
+  static constexpr int SB = 3;
+  static constexpr int SG = PB ? SB : SA;               // log2 rows per group
+  static constexpr int kGroupRows = 1 << SG;
+  __host__ __device__ static constexpr int row(int r) { return RB * r + PA * (r >> SA) + (PB ? PB * (r >> SB) : 0); }
+  static constexpr int kGroupBytes = row(kGroupRows);   // bytes from one group to the next
+  static_assert(kGroupBytes % 16 == 0 && 16 % kGroupRows == 0, "groups of whole granules within 16 rows");
+};
 
 template <class Tr, int D, int QW, int NW, int BC>
 struct Shape {
@@ -203,16 +214,22 @@ struct Shape {
   static constexpr int kRV = D * Tr::kEV;     // bytes per V row
   static constexpr int kCK = kRK / 16;        // 16-byte chunks per K row
   static constexpr int kCV = kRV / 16;
-  static constexpr int kSK = BC * kRK;        // bytes per K stage
-  static constexpr int kSV = BC * kRV;
-  static constexpr int kBlkK = kSK / 1024;    // 1 KiB direct-load blocks per K stage
-  static constexpr int kBlkV = kSV / 1024;
+  static constexpr int kRSK = kRK + 16;       // LDS bytes per K row (one pad granule)
+  static constexpr int kGK = kCK + 1;         // LDS granules per K row
+  static constexpr int kGranK = BC * kGK;     // LDS granules per K stage
+  static constexpr int kSK = BC * kRSK;       // bytes per K stage
+  using VL = VLayout<kRV, Tr::kFp8>;
+  static constexpr int kGV = VL::kGroupBytes / 16;         // LDS granules per group of V rows
+  static constexpr int kGranV = BC / VL::kGroupRows * kGV;  // LDS granules per V stage
+  static constexpr int kSV = kGranV * 16;                   // bytes per V stage
+  static constexpr int kBlkK = (kGranK + 63) / 64;  // direct-load instructions (64 granules each) per K stage
+  static constexpr int kBlkV = (kGranV + 63) / 64;
   static constexpr int kQSteps = Tr::kFp8 ? D / 64 : D / 16;  // QK instructions per 32x32 block
   static constexpr int kKReads = kKB * kQSteps * (Tr::kFp8 ? 2 : 1);  // 128-bit LDS reads of K per tile
   static constexpr int kQKMfma = kKB * kQSteps * kQB;                 // Q K^T instructions per tile
   static constexpr int kExpVALU = kKB * kQB * 16 * 3;                   // approx. vector instructions of exp_tile
   static constexpr int kVReads = kDB * kKB * 2 * (Tr::kFp8 ? 1 : 2);    // transposing LDS reads of V per tile
-  static_assert(kSK % 1024 == 0 && kSV % 1024 == 0, "stage must be whole 1 KiB blocks");
+  static_assert(BC % 32 == 0, "whole 32-key blocks");
 };
 
 }  // namespace
@@ -231,10 +248,10 @@ __global__ __launch_bounds__(NW * 64, WPE) void fa_fwd_kernel(FwdParams p) {
   // Two LDS stages.  Separate arrays let the compiler tell the
   // direct-to-LDS loads of one stage from the reads of the other (with one
   // array and computed offsets it waits for every load before any read).
-  __shared__ __attribute__((aligned(1024))) char lds_k0[S::kSK];
-  __shared__ __attribute__((aligned(1024))) char lds_k1[S::kSK];
-  __shared__ __attribute__((aligned(1024))) char lds_v0[S::kSV];
-  __shared__ __attribute__((aligned(1024))) char lds_v1[S::kSV];
+  __shared__ __attribute__((aligned(16))) char lds_k0[S::kSK];
+  __shared__ __attribute__((aligned(16))) char lds_k1[S::kSK];
+  __shared__ __attribute__((aligned(16))) char lds_v0[S::kSV];
+  __shared__ __attribute__((aligned(16))) char lds_v1[S::kSV];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -289,20 +306,19 @@ __global__ __launch_bounds__(NW * 64, WPE) void fa_fwd_kernel(FwdParams p) {
   const int n_all = (N + BC - 1) / BC;
   const int n_kv = CAUSAL ? min(n_all, (q0 + S::kBR - 1) / BC + 1) : n_all;
 
-  // ---- direct HBM -> LDS tile loads.  Lane L of a 1 KiB block instruction
-  // writes LDS granule 64*blk + L; it fetches the logical chunk that the
-  // swizzle places there.
+  // ---- direct HBM -> LDS tile loads.  Lane L of direct-load instruction
+  // `blk` writes LDS granule 64*blk + L of the stage; it fetches the chunk of
+  // the tile that the layout places there, and pad granules (and granules past
+  // the stage) are left alone.  The per-lane source offsets are fixed for the
+  // whole kernel; only the tile's first key moves.
   auto issue_k = [&](int kt, char* dk) __attribute__((always_inline)) {
     const int k0 = kt * BC;
 #pragma unroll
     for (int j = 0; j < (S::kBlkK + NW - 1) / NW; ++j) {
       const int blk = wave + j * NW;
-      if (blk < S::kBlkK) {
-        const int g = blk * 64 + lane;
-        const int r = g / S::kCK, pc = g % S::kCK;
-        const int lc = pc ^ swz<S::kRK>(r);
-        load_lds16(rk, dk + blk * 1024, (k0 + r) * S::kRK + lc * 16);
-      }
+      const int g = blk * 64 + lane;
+      const int r = g / S::kGK, c = g - r * S::kGK;
+      if (blk < S::kBlkK && g < S::kGranK && c < S::kCK) load_lds16(rk, dk + blk * 1024, (k0 + r) * S::kRK + c * 16);
     }
   };
   auto issue_v = [&](int kt, char* dv) __attribute__((always_inline)) {
@@ -310,12 +326,17 @@ __global__ __launch_bounds__(NW * 64, WPE) void fa_fwd_kernel(FwdParams p) {
 #pragma unroll
     for (int j = 0; j < (S::kBlkV + NW - 1) / NW; ++j) {
       const int blk = wave + j * NW;
-      if (blk < S::kBlkV) {
-        const int g = blk * 64 + lane;
-        const int r = g / S::kCV, pc = g % S::kCV;
-        const int lc = pc ^ swz<S::kRV>(r);
-        load_lds16(rv, dv + blk * 1024, (k0 + r) * S::kRV + lc * 16);
-      }
+      const int g = blk * 64 + lane;
+      const int grp = g / S::kGV;
+      const int off = (g - grp * S::kGV) * 16;  // byte offset inside the group of rows
+      int r = -1, c = 0;
+#pragma unroll
+      for (int i = 0; i < S::VL::kGroupRows; ++i)
+        if (off >= S::VL::row(i) && off < S::VL::row(i) + S::kRV) {
+          r = grp * S::VL::kGroupRows + i;
+          c = (off - S::VL::row(i)) / 16;
+        }
+      if (blk < S::kBlkV && g < S::kGranV && r >= 0) load_lds16(rv, dv + blk * 1024, (k0 + r) * S::kRV + c * 16);
     }
   };
 
@@ -345,24 +366,27 @@ __global__ __launch_bounds__(NW * 64, WPE) void fa_fwd_kernel(FwdParams p) {
   u32x2 vop8[S::kDB][S::kKB][Tr::kFp8 ? 2 : 1];
 
   // ---- K operands: lane (half, l32) of block kb reads key row 32*kb + l32,
-  // k-group `half` of each instruction step.
+  // k-group `half` of each instruction step (two 16-byte chunks for 8-bit
+  // values, one otherwise).
+  const int kbase = l32 * S::kRSK + half * (Tr::kFp8 ? 32 : 16);
+  auto k_read16 = [&](const char* lk, int kb, int s) __attribute__((always_inline)) {
+    return lds_read_b128(lk, kbase + 32 * kb * S::kRSK + 32 * s);
+  };
+  auto k_read8 = [&](const char* lk, int kb, int s) __attribute__((always_inline)) {
+    const u32x4 a0 = lds_read_b128(lk, kbase + 32 * kb * S::kRSK + 64 * s);
+    const u32x4 a1 = lds_read_b128(lk, kbase + 32 * kb * S::kRSK + 64 * s + 16);
+    return i32x8{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+  };
   auto load_k = [&](const char* lk) __attribute__((always_inline)) {
 #pragma unroll
-    for (int kb = 0; kb < S::kKB; ++kb) {
-      const int r = kb * 32 + l32;
-      const int sw = swz<S::kRK>(r);
+    for (int kb = 0; kb < S::kKB; ++kb)
 #pragma unroll
       for (int s = 0; s < S::kQSteps; ++s) {
-        if constexpr (Tr::kFp8) {
-          const u32x4 a0 = lds_read_b128(lk, (r * S::kCK + ((4 * s + 2 * half) ^ sw)) * 16);
-          const u32x4 a1 = lds_read_b128(lk, (r * S::kCK + ((4 * s + 2 * half + 1) ^ sw)) * 16);
-          kop8[kb][s] = i32x8{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
-                              (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
-        } else {
-          kop16[kb][s] = lds_read_b128(lk, (r * S::kCK + ((2 * s + half) ^ sw)) * 16);
-        }
+        if constexpr (Tr::kFp8)
+          kop8[kb][s] = k_read8(lk, kb, s);
+        else
+          kop16[kb][s] = k_read16(lk, kb, s);
       }
-    }
   };
 
   // ---- S^T = K Q^T into `dst`
@@ -470,28 +494,40 @@ __global__ __launch_bounds__(NW * 64, WPE) void fa_fwd_kernel(FwdParams p) {
   // ---- V^T operands.  Element e of lane (half, col) of the V^T operand is
   // V[32*kb + 16*t + 8*(e/4) + 4*half + e%4][col], matching the key held in
   // element e of the P operand (accumulator row 8*t + e of the S^T block).
-  auto load_v = [&](const char* lv) __attribute__((always_inline)) {
+  // 16-bit values: lane (g, u) = (lane / 16, lane % 16) reads 4 values of
+  // columns 32*db + 16*(g%2) + 4*(u%4) from rows r0 = 32*kb + 16*t + 4*half +
+  // u/4 and r0 + 8.  8-bit values: 8 keys of byte column 32*db + 16*(g%2) +
+  // 8*(u%2) from the rows listed above, e = u/2.  Rows 32*kb + 16*t start a
+  // group of the layout, so their offsets are compile-time constants.
+  const int vbase = [&] {
     const int g = lane >> 4, u = lane & 15;
+    if constexpr (Tr::kFp8) {
+      const int ep = u >> 1;
+      return S::VL::row(8 * (ep >> 2) + 4 * half + (ep & 3)) + 16 * (g & 1) + 8 * (u & 1);
+    } else {
+      return S::VL::row(4 * half + (u >> 2)) + 2 * (16 * (g & 1) + 4 * (u & 3));
+    }
+  }();
+  auto v_read16 = [&](const char* lv, int db, int kb, int t) __attribute__((always_inline)) {
+    const int o = vbase + S::VL::row(32 * kb + 16 * t) + 64 * db;
+    const u32x2 lo = lds_read_tr16(lv, o);
+    const u32x2 hi = lds_read_tr16(lv, o + S::VL::row(8));
+    return u32x4{lo[0], lo[1], hi[0], hi[1]};
+  };
+  auto v_read8 = [&](const char* lv, int db, int kb, int t) __attribute__((always_inline)) {
+    return lds_read_tr8(lv, vbase + S::VL::row(32 * kb + 16 * t) + 32 * db);
+  };
+  auto load_v = [&](const char* lv) __attribute__((always_inline)) {
 #pragma unroll
     for (int db = 0; db < S::kDB; ++db)
 #pragma unroll
       for (int kb = 0; kb < S::kKB; ++kb)
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-          if constexpr (Tr::kFp8) {
-            // 8 keys of one byte column per lane from the 8-bit transposing read
-            const int col = 32 * db + 16 * (g & 1) + 8 * (u & 1);  // byte column this lane addresses
-            const int ep = u >> 1;
-            const int row = kb * 32 + 16 * t + 8 * (ep >> 2) + 4 * half + (ep & 3);
-            vop8[db][kb][t] = lds_read_tr8(lv, (row * S::kCV + ((col >> 4) ^ swz<S::kRV>(row))) * 16 + (col & 15));
-          } else {
-            const int col = 32 * db + 16 * (g & 1) + 4 * (u & 3);  // element column this lane addresses
-            const int r0 = kb * 32 + 16 * t + 4 * half + (u >> 2);
-            const int r1 = r0 + 8;
-            const u32x2 lo = lds_read_tr16(lv, (r0 * S::kCV + ((col >> 3) ^ swz<S::kRV>(r0))) * 16 + (col & 7) * 2);
-            const u32x2 hi = lds_read_tr16(lv, (r1 * S::kCV + ((col >> 3) ^ swz<S::kRV>(r1))) * 16 + (col & 7) * 2);
-            vop16[db][kb][t] = u32x4{lo[0], lo[1], hi[0], hi[1]};
-          }
+          if constexpr (Tr::kFp8)
+            vop8[db][kb][t] = v_read8(lv, db, kb, t);
+          else
+            vop16[db][kb][t] = v_read16(lv, db, kb, t);
         }
   };
 
@@ -527,19 +563,14 @@ __global__ __launch_bounds__(NW * 64, WPE) void fa_fwd_kernel(FwdParams p) {
     for (int kb = 0; kb < S::kKB; ++kb) {
 #pragma unroll
       for (int qb = 0; qb < S::kQB; ++qb) sacc[kb][qb] = f32x16{};
-      const int r = kb * 32 + l32;
-      const int sw = swz<S::kRK>(r);
 #pragma unroll
       for (int s = 0; s < S::kQSteps; ++s) {
         if constexpr (Tr::kFp8) {
-          const u32x4 a0 = lds_read_b128(lk, (r * S::kCK + ((4 * s + 2 * half) ^ sw)) * 16);
-          const u32x4 a1 = lds_read_b128(lk, (r * S::kCK + ((4 * s + 2 * half + 1) ^ sw)) * 16);
-          const i32x8 a = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
-                           (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+          const i32x8 a = k_read8(lk, kb, s);
 #pragma unroll
           for (int qb = 0; qb < S::kQB; ++qb) sacc[kb][qb] = mfma_fp8(a, q8[qb][s], sacc[kb][qb]);
         } else {
-          const u32x4 a = lds_read_b128(lk, (r * S::kCK + ((2 * s + half) ^ sw)) * 16);
+          const u32x4 a = k_read16(lk, kb, s);
 #pragma unroll
           for (int qb = 0; qb < S::kQB; ++qb) sacc[kb][qb] = mfma16(a, q16[qb][s], sacc[kb][qb], kBf);
         }

@@ -62,10 +62,19 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     x = np.ascontiguousarray(x, dtype=np.float32)
     if not np.isfinite(x).all():
         raise ValueError("bf16 rounding expects finite inputs")
-    bits = x.view(np.uint32).astype(np.uint64)
-    lsb = (bits >> 16) & 1
-    rounded = (bits + 0x7FFF + lsb) >> 16
-    return rounded.astype(np.uint16)
+    # finite float32 bit patterns stay below 2^32 after adding 0x8000, so
+    # uint32 arithmetic cannot wrap; work in chunks to bound temporaries
+    flat = x.reshape(-1)
+    out = np.empty(flat.shape, np.uint16)
+    step = 1 << 24
+    for i in range(0, flat.size, step):
+        bits = flat[i:i + step].view(np.uint32).copy()
+        lsb = (bits >> 16) & 1
+        bits += 0x7FFF
+        bits += lsb
+        bits >>= 16
+        out[i:i + step] = bits
+    return out.reshape(x.shape)
 
 
 def quantize_e4m3(x: np.ndarray) -> tuple[np.ndarray, float]:
