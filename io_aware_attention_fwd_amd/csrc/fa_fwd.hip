@@ -26,7 +26,8 @@
 //   * K and V tiles go HBM -> LDS with buffer loads that write LDS directly
 //     (no registers, out-of-range rows read as zero), double buffered: tile
 //     t+1 is in flight while tile t is computed; one barrier per tile.
-//   * The 16-byte chunks of each LDS row are XOR-swizzled by row.
+//   * LDS rows are padded so that operand reads are free of bank conflicts
+//     and need no per-read address arithmetic.
 //   * Rescaling is lazy and exact: the reference maximum of a row only moves
 //     when a tile's maximum exceeds it by more than 2^8 in the exp2 domain,
 //     so probabilities stay below 256 and the accumulators are rescaled a few
@@ -203,6 +204,37 @@ struct VLayout {
   static constexpr int kGroupBytes = row(kGroupRows);   // bytes from one group to the next
   static_assert(kGroupBytes % 16 == 0 && 16 % kGroupRows == 0, "groups of whole granules within 16 rows");
 };
+
+// Software pipeline over a fixed sequence of N matrix instructions whose A
+// operands come from LDS: the operand of instruction i + DEPTH is read right
+// after instruction i issues, so every read has DEPTH instructions' time to
+// land.  Instructions [0, NPV) take two operand reads each, the rest one.
+// The sched_group_barrier sequence pins that order through scheduling (left
+// alone, the scheduler sinks each read next to its use).
+template <int I, int N, int NPV, int DEPTH>
+__device__ __forceinline__ void pipeline_order() {
+  if constexpr (I < N) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one matrix instruction
+    if constexpr (I + DEPTH < N) __builtin_amdgcn_sched_group_barrier(0x100, I + DEPTH < NPV ? 2 : 1, 0);  // its reads
+    pipeline_order<I + 1, N, NPV, DEPTH>();
+  }
+}
+
+template <int N, int NPV, int DEPTH, class Read, class Mma>
+__device__ __forceinline__ void op_pipeline(Read read, Mma mma) {
+  u32x4 buf[DEPTH];
+  constexpr int P = DEPTH < N ? DEPTH : N;
+#pragma unroll
+  for (int i = 0; i < P; ++i) buf[i] = read(i);
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    mma(i, buf[i % DEPTH]);
+    if (i + DEPTH < N) buf[i % DEPTH] = read(i + DEPTH);
+  }
+  constexpr int kPro = (P < NPV ? P : NPV) * 2 + (P > NPV ? P - NPV : 0);
+  __builtin_amdgcn_sched_group_barrier(0x100, kPro, 0);  // the first DEPTH operands' reads
+  pipeline_order<0, N, NPV, DEPTH>();
+}
 
 template <class Tr, int D, int QW, int NW, int BC>
 struct Shape {
@@ -582,8 +614,13 @@ __global__ __launch_bounds__(NW * 64, WPE) void fa_fwd_kernel(FwdParams p) {
     mma_pv();
   };
 
-  // A wave works on tile kt only if some of its rows can see a key of it.
-  auto active = [&](int kt) __attribute__((always_inline)) { return kt >= 0 && kt < n_kv && !(CAUSAL && kt * BC > qw0 + QW - 1); };
+  // A wave works on tile kt only if some of its rows exist and can see a key
+  // of it.  (The row test also keeps the branch per-wave in the compiler's
+  // eyes; with a workgroup-uniform branch it hoists work across the matrix
+  // phase's alternatives and runs out of registers at d = 128.)
+  auto active = [&](int kt) __attribute__((always_inline)) {
+    return kt >= 0 && kt < n_kv && qw0 < N && !(CAUSAL && kt * BC > qw0 + QW - 1);
+  };
 
   // ---- main loop: ping-pong between the two waves of each SIMD.
   // Waves 0-3 (group 0) and 4-7 (group 1) share the four SIMDs pairwise.
@@ -597,9 +634,52 @@ __global__ __launch_bounds__(NW * 64, WPE) void fa_fwd_kernel(FwdParams p) {
   // 2t+2..2t+3.  Both are issued at phase 2t (K one tile ahead) and waited for
   // at the end of phase 2t+1.
   const int group = wave >> 2;
+  // Matrix phase: P V of the previous tile, then Q K^T of this one.  For
+  // 16-bit types both run as one pipelined stream of instructions (P V in
+  // (kb, t, db) order, db fastest, so consecutive instructions feed
+  // different accumulators; Q K^T in (step, kb) order).  The wave raises its
+  // issue priority for the phase: the other wave of its SIMD is running the
+  // vector-heavy softmax, and the matrix stream should not wait behind it.
+  constexpr int kNPV = S::kDB * S::kKB * 2;
+  constexpr int kNQK = S::kKB * S::kQSteps;
+  constexpr int kDepth = 4;
+  auto pv_op = [&](int i, u32x4 a) __attribute__((always_inline)) {
+    const int db = i % S::kDB, t = (i / S::kDB) % 2, kb = i / (2 * S::kDB);
+#pragma unroll
+    for (int qb = 0; qb < S::kQB; ++qb) oacc[db][qb] = mfma16(a, pb[kb][qb][t], oacc[db][qb], kBf);
+  };
+  auto qk_op = [&](int i, u32x4 a) __attribute__((always_inline)) {
+    const int kb = i % S::kKB, st = i / S::kKB;
+#pragma unroll
+    for (int qb = 0; qb < S::kQB; ++qb) sacc[kb][qb] = mfma16(a, q16[qb][st], st == 0 ? f32x16{} : sacc[kb][qb], kBf);
+  };
+  auto pv_rd = [&](const char* lv, int i) __attribute__((always_inline)) {
+    return v_read16(lv, i % S::kDB, i / (2 * S::kDB), (i / S::kDB) % 2);
+  };
+  auto qk_rd = [&](const char* lk, int i) __attribute__((always_inline)) { return k_read16(lk, i % S::kKB, i / S::kKB); };
   auto mfma_phase = [&](int kt, const char* lk, const char* lv_prev) __attribute__((always_inline)) {
-    if (active(kt - 1)) pv_interleaved(lv_prev);
-    if (active(kt)) qk_interleaved(lk);
+    __builtin_amdgcn_s_setprio(1);
+    const bool a_pv = active(kt - 1), a_qk = active(kt);
+    if constexpr (Tr::kFp8) {
+      if (a_pv) pv_interleaved(lv_prev);
+      if (a_qk) qk_interleaved(lk);
+    } else if (a_pv && a_qk) {
+      op_pipeline<kNPV + kNQK, kNPV, kDepth>(
+          [&](int i) __attribute__((always_inline)) { return i < kNPV ? pv_rd(lv_prev, i) : qk_rd(lk, i - kNPV); },
+          [&](int i, u32x4 a) __attribute__((always_inline)) {
+            if (i < kNPV)
+              pv_op(i, a);
+            else
+              qk_op(i - kNPV, a);
+          });
+    } else if (a_pv) {
+      op_pipeline<kNPV, kNPV, kDepth>([&](int i) __attribute__((always_inline)) { return pv_rd(lv_prev, i); },
+                                      [&](int i, u32x4 a) __attribute__((always_inline)) { pv_op(i, a); });
+    } else if (a_qk) {
+      op_pipeline<kNQK, 0, kDepth>([&](int i) __attribute__((always_inline)) { return qk_rd(lk, i); },
+                                   [&](int i, u32x4 a) __attribute__((always_inline)) { qk_op(i, a); });
+    }
+    __builtin_amdgcn_s_setprio(0);
   };
   auto tile_step = [&](int kt, const char* lk, const char* lv_prev, char* k_next, char* v_cur) __attribute__((always_inline)) {
     if (kt + 1 < n_kv) issue_k(kt + 1, k_next);
