@@ -259,8 +259,6 @@ struct Shape {
   static constexpr int kQSteps = Tr::kFp8 ? D / 64 : D / 16;  // QK instructions per 32x32 block
   static constexpr int kKReads = kKB * kQSteps * (Tr::kFp8 ? 2 : 1);  // 128-bit LDS reads of K per tile
   static constexpr int kQKMfma = kKB * kQSteps * kQB;                 // Q K^T instructions per tile
-  static constexpr int kExpVALU = kKB * kQB * 16 * 3;                   // approx. vector instructions of exp_tile
-  static constexpr int kVReads = kDB * kKB * 2 * (Tr::kFp8 ? 1 : 2);    // transposing LDS reads of V per tile
   static_assert(BC % 32 == 0, "whole 32-key blocks");
 };
 
@@ -269,8 +267,7 @@ struct Shape {
 // The kernel template has external linkage so that every instantiation's
 // host-side launch stub is emitted.
 // SCHED: 0 = plain (every wave runs Q K^T, softmax, P V of a tile in turn),
-//        1 = ping-pong between wave groups, 2 = software pipeline inside each
-//        wave (Q K^T of the next tile interleaved with the softmax of this one).
+//        1 = ping-pong between wave groups.
 template <class Tr, int D, bool CAUSAL, int QW, int NW, int BC, int SCHED, int WPE>
 __global__ __launch_bounds__(NW * 64, WPE) void fa_fwd_kernel(FwdParams p) {
   constexpr bool PP = SCHED == 1;
@@ -707,52 +704,6 @@ __global__ __launch_bounds__(NW * 64, WPE) void fa_fwd_kernel(FwdParams p) {
       tile_step(kt, lds_k0, lds_v1, lds_k1, lds_v0);
       if (kt + 1 <= n_kv) tile_step(kt + 1, lds_k1, lds_v0, lds_k0, lds_v1);
     }
-  } else if constexpr (SCHED == 2) {
-    // Software pipeline inside each wave: while the softmax of tile t runs on
-    // the vector units, Q K^T of tile t+1 runs on the matrix cores; the two
-    // are interleaved in one instruction stream.  K(t) sits in stage t%2 for
-    // steps t-1 and t, V(t) in stage t%2 for step t; both are issued one step
-    // ahead.
-    f32x16 sacc2[S::kKB][S::kQB];
-    auto pl_step = [&](int kt, SArr& s_cur, SArr& s_next, const char* k_next, const char* v_cur, char* k_dst,
-                       char* v_dst) __attribute__((always_inline)) {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();  // K(kt+1) and V(kt) landed; the stages written below are no longer read
-      if (kt + 2 < n_kv) issue_k(kt + 2, k_dst);
-      if (kt + 1 < n_kv) issue_v(kt + 1, v_dst);
-      // No per-wave skipping here: a wave whose rows all precede tile kt
-      // sees only masked scores (P = 0, nothing changes), and Q K^T of a
-      // tile past the end reads a stale stage whose result is never used.
-      // Keeping the step branch-free keeps the softmax and the matrix
-      // instructions in one basic block, where they can be interleaved.
-      load_k(k_next);
-      mask_tile(kt, s_cur);
-      max_rescale(s_cur);
-      load_v(v_cur);
-      exp_tile(s_cur);
-      mma_qk_into(s_next);
-      // V operand reads first, then one matrix instruction and a slice of
-      // the vector work, repeated
-      __builtin_amdgcn_sched_group_barrier(0x100, S::kVReads, 0);
-#pragma unroll
-      for (int i = 0; i < S::kQKMfma; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, S::kExpVALU / S::kQKMfma, 0);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      mma_pv();
-    };
-    issue_k(0, lds_k0);
-    issue_v(0, lds_v0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (n_kv > 1) issue_k(1, lds_k1);
-    load_k(lds_k0);
-    mma_qk_into(sacc);
-    for (int kt = 0; kt < n_kv; kt += 2) {
-      pl_step(kt, sacc, sacc2, lds_k1, lds_v0, lds_k0, lds_v1);
-      if (kt + 1 < n_kv) pl_step(kt + 1, sacc2, sacc, lds_k0, lds_v1, lds_k1, lds_v0);
-    }
   } else {
     // Plain schedule: every wave runs Q K^T, softmax and P V of a tile in
     // turn; with several workgroups per CU the waves of different
@@ -825,15 +776,17 @@ hipError_t launch_one(const FwdParams& p, hipStream_t stream) {
 // selects one of them instead of the default (tile sweeps only; an unknown
 // value falls back to the default).
 constexpr Variant kVariants[] = {{32, 8, 64, 1, 2}, {32, 4, 64, 0, 4}, {32, 4, 64, 0, 3}, {32, 4, 64, 0, 2},
-                                 {32, 4, 64, 2, 2}, {64, 4, 64, 0, 2}};
+                                 {64, 4, 64, 0, 2}};
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
 // Measured on MI355X (A/B in one process): the ping-pong schedule wins at
-// d = 128; at d = 64 the plain schedule, with 64 rows per wave for long
-// non-causal sequences and 32 rows per wave at three waves per SIMD otherwise.
+// d = 128 for 16-bit types (fp8, with half the operand bytes, prefers the
+// plain schedule at three waves per SIMD); at d = 64 the plain schedule, with
+// 64 rows per wave for long non-causal sequences and 32 rows per wave at
+// three waves per SIMD otherwise.
 int default_variant(Dtype dt, int d, bool causal, int N) {
-  if (d == 128) return dt == Dtype::FP8 ? 3 : 0;  // plain at two waves per SIMD for fp8, else ping-pong
-  if (!causal && N >= 2048) return 5;     // 64 rows per wave: half the LDS operand traffic per FLOP
+  if (d == 128) return dt == Dtype::FP8 ? 2 : 0;  // plain at three waves per SIMD for fp8, else ping-pong
+  if (!causal && N >= 2048) return 4;     // 64 rows per wave: half the LDS operand traffic per FLOP
   return 2;                               // plain, three waves per SIMD
 }
 
@@ -856,8 +809,7 @@ hipError_t dispatch_variant(int v, const FwdParams& p, hipStream_t stream) {
     case 1: return launch_one<Tr, D, CAUSAL, 32, 4, 64, 0, 4>(p, stream);
     case 2: return launch_one<Tr, D, CAUSAL, 32, 4, 64, 0, 3>(p, stream);
     case 3: return launch_one<Tr, D, CAUSAL, 32, 4, 64, 0, 2>(p, stream);
-    case 4: return launch_one<Tr, D, CAUSAL, 32, 4, 64, 2, 2>(p, stream);
-    case 5: return launch_one<Tr, D, CAUSAL, 64, 4, 64, 0, 2>(p, stream);
+    case 4: return launch_one<Tr, D, CAUSAL, 64, 4, 64, 0, 2>(p, stream);
     default: return launch_one<Tr, D, CAUSAL, 32, 8, 64, 1, 2>(p, stream);
   }
 }
