@@ -119,6 +119,25 @@ def make(B: int, H: int, N: int, d: int, dtype: str, seed: int = 0) -> Inputs:
     return store(dtype, q, k, v)
 
 
+def make_packed(lengths, H: int, d: int, dtype: str, seed: int = 0):
+    """Sequences of the given lengths packed back to back: Q, K, V of shape
+    [total, H, d] (N(0,1) draws from ``seed`` in the order Q, K, V, stored as
+    ``dtype``) and the B+1 row offsets as an int32 array."""
+    lengths = [int(n) for n in lengths]
+    if any(n < 0 for n in lengths):
+        raise ValueError("sequence lengths must be >= 0")
+    total = sum(lengths)
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    rng = np.random.default_rng(seed)
+    q, k, v = (rng.standard_normal(size=(total, H, d), dtype=np.float32) for _ in range(3))
+    return store(dtype, q, k, v), cu
+
+
+def length_mix(count: int, lo: int, hi: int, seed: int = 0):
+    """``count`` sequence lengths drawn uniformly from [lo, hi] (inclusive)."""
+    return [int(n) for n in np.random.default_rng(seed).integers(lo, hi + 1, size=count)]
+
+
 def structured(B: int, H: int, N: int, d: int, dtype: str, period: int = 64) -> Inputs:
     """Inputs whose exact output is known row by row.
 

@@ -16,7 +16,8 @@ forms, invariants, an mpmath brute force, torch's float64 CPU attention and a
 mutation check); see the module docstrings for the passages followed.
 """
 from .formats import decode, decode_e4m3, decode_bf16_bits, dequantize
-from .attention import attention_slice, attention, slice_sample
+from .attention import attention_slice, attention, attention_varlen, slice_sample
+from .backward import attention_backward_slice, attention_backward
 
 __all__ = [
     "decode",
@@ -25,5 +26,8 @@ __all__ = [
     "dequantize",
     "attention_slice",
     "attention",
+    "attention_varlen",
     "slice_sample",
+    "attention_backward_slice",
+    "attention_backward",
 ]

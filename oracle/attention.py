@@ -32,6 +32,16 @@ Passages followed:
 
 The score matrix is built ``row_chunk`` query rows at a time only to bound
 memory; each chunk is the plain definition above.
+
+``attention_varlen`` applies the same definition to sequences of different
+lengths packed back to back ([total, H, d], sequence b owning rows
+cu[b]..cu[b+1]-1): every (sequence, head) is its own attention problem, and
+a causal row sees the keys of its own sequence up to itself.  The pages pad
+unaligned lengths (page "从RTX 3090到H100：FlashAttention在NVIDIA各代GPU架构上
+的性能全景分析", section 3.2, common pitfalls item 2) and name dynamic shapes as
+a direction (page "FlashAttention与TensorRT 10集成", section "推理优化的未来方
+向" item 1); computing each sequence on its own rows is what padding with
+masked keys would give for the rows that exist.
 """
 from __future__ import annotations
 
@@ -95,4 +105,25 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, causal:
     todo = slices if slices is not None else [(b, h) for b in range(B) for h in range(H)]
     for b, h in todo:
         o[b, h], lse[b, h] = attention_slice(q[b, h], k[b, h], v[b, h], scale, causal, row_chunk)
+    return o, lse
+
+
+def attention_varlen(q: np.ndarray, k: np.ndarray, v: np.ndarray, cu, scale: float, causal: bool,
+                     sequences=None, row_chunk: int = 1024):
+    """Packed [total, H, d] float64 inputs and B+1 offsets ``cu`` -> (O [total,H,d], lse [H,total]).
+
+    With ``sequences`` (a list of sequence indices), only those are computed;
+    the rows of the others stay NaN.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    total, H, d = q.shape
+    cu = [int(x) for x in cu]
+    o = np.full((total, H, v.shape[-1]), np.nan, dtype=np.float64)
+    lse = np.full((H, total), np.nan, dtype=np.float64)
+    todo = sequences if sequences is not None else range(len(cu) - 1)
+    for b in todo:
+        r0, r1 = cu[b], cu[b + 1]
+        for h in range(H):
+            o[r0:r1, h], lse[h, r0:r1] = attention_slice(q[r0:r1, h], k[r0:r1, h], v[r0:r1, h], scale, causal,
+                                                         row_chunk)
     return o, lse

@@ -189,3 +189,137 @@ def pin_invariants(impl):
 
 
 ALL_PINS = (pin_closed_forms, pin_invariants, pin_torch_sdpa, pin_brute_force)
+
+
+# ------------------------------------------------------------- packed batches
+# ``impl_varlen(q, k, v, cu, scale, causal) -> (O [total,H,d], lse [H,total])``
+# on packed float64 [total, H, d] inputs.
+
+def _packed(rng, lengths, H, d, scale=1.0):
+    total = int(sum(lengths))
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    mk = lambda: (rng.standard_normal((total, H, d)) * scale).astype(np.float16).astype(np.float64)
+    return mk(), mk(), mk(), cu
+
+
+def pin_varlen_brute_force(impl_varlen):
+    """Every (sequence, head) against the mpmath loops on that sequence's rows
+    alone; lengths include empty sequences and single rows."""
+    if mpmath is None:  # pragma: no cover
+        return
+    rng = np.random.default_rng(5)
+    lengths = [3, 0, 1, 6, 2]
+    H, d = 2, 4
+    q, k, v, cu = _packed(rng, lengths, H, d, 1.5)
+    for causal in (False, True):
+        o, lse = impl_varlen(q, k, v, cu, 0.45, causal)
+        assert o.shape == q.shape and lse.shape == (H, q.shape[0])
+        for b in range(len(lengths)):
+            r0, r1 = cu[b], cu[b + 1]
+            for h in range(H):
+                ob, lb = brute_force(q[r0:r1, h], k[r0:r1, h], v[r0:r1, h], 0.45, causal)
+                assert np.allclose(o[r0:r1, h], ob, rtol=0, atol=1e-12), (b, h, causal)
+                assert np.allclose(lse[h, r0:r1], lb, rtol=0, atol=1e-12), (b, h, causal)
+
+
+def pin_varlen_equal_lengths_are_dense(impl_varlen):
+    """Equal lengths: the packed problem is the dense [B, H, N, d] one, whose
+    oracle is pinned on its own."""
+    from oracle import attention as dense_attention
+
+    rng = np.random.default_rng(6)
+    B, N, H, d = 3, 9, 2, 8
+    q, k, v, cu = _packed(rng, [N] * B, H, d)
+    dense = lambda x: x.reshape(B, N, H, d).transpose(0, 2, 1, 3)
+    for causal in (False, True):
+        o, lse = impl_varlen(q, k, v, cu, 0.3, causal)
+        od, ld = dense_attention(dense(q), dense(k), dense(v), 0.3, causal)
+        assert np.allclose(dense(o), od, rtol=0, atol=1e-13)
+        assert np.allclose(lse.reshape(H, B, N).transpose(1, 0, 2), ld, rtol=0, atol=1e-12)
+
+
+def pin_varlen_sequence_order(impl_varlen):
+    """Reordering the packed sequences reorders the outputs block by block: no
+    row sees another sequence."""
+    rng = np.random.default_rng(7)
+    lengths = [5, 1, 8, 3]
+    H, d = 2, 8
+    q, k, v, cu = _packed(rng, lengths, H, d)
+    o, lse = impl_varlen(q, k, v, cu, 0.25, True)
+    order = [2, 0, 3, 1]
+    rows = np.concatenate([np.arange(cu[b], cu[b + 1]) for b in order])
+    cu2 = np.concatenate([[0], np.cumsum([lengths[b] for b in order])])
+    o2, lse2 = impl_varlen(q[rows], k[rows], v[rows], cu2, 0.25, True)
+    assert np.allclose(o2, o[rows], rtol=0, atol=1e-13)
+    assert np.allclose(lse2, lse[:, rows], rtol=0, atol=1e-12)
+
+
+VARLEN_PINS = (pin_varlen_brute_force, pin_varlen_equal_lengths_are_dense, pin_varlen_sequence_order)
+
+
+# ------------------------------------------------------------------ backward
+# ``impl_bwd(q, k, v, do, scale, causal) -> (dQ, dK, dV)`` on float64 [N, d]
+# slices; the forward oracle (pinned above) defines the function differentiated.
+
+def pin_bwd_finite_differences(impl_bwd):
+    """Central differences of L = sum(dO * O) through the forward oracle."""
+    from oracle import attention_slice
+
+    rng = np.random.default_rng(21)
+    for n, d, scale, causal in [(4, 3, 0.7, False), (5, 2, -0.4, True), (1, 3, 0.5, True), (6, 4, 1.1, True)]:
+        q, k, v, do = (rng.standard_normal((n, d)) for _ in range(4))
+        dq, dk, dv = impl_bwd(q, k, v, do, scale, causal)
+        loss = lambda qq, kk, vv: float((attention_slice(qq, kk, vv, scale, causal)[0] * do).sum())
+        eps = 1e-6
+        for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+            num = np.zeros_like(x)
+            for idx in np.ndindex(*x.shape):
+                xp, xm = x.copy(), x.copy()
+                xp[idx] += eps
+                xm[idx] -= eps
+                args_p = {"q": q, "k": k, "v": v}
+                args_m = dict(args_p)
+                args_p[name], args_m[name] = xp, xm
+                num[idx] = (loss(args_p["q"], args_p["k"], args_p["v"]) - loss(args_m["q"], args_m["k"], args_m["v"])) / (2 * eps)
+            assert np.allclose(g, num, rtol=1e-6, atol=1e-7), (name, n, d, causal, np.abs(g - num).max())
+
+
+def pin_bwd_torch_autograd(impl_bwd):
+    """torch autograd in float64 on the CPU through explicit softmax attention."""
+    rng = np.random.default_rng(22)
+    for n, d, scale, causal in [(7, 8, 0.35, False), (9, 4, 0.8, True), (16, 16, 0.25, True)]:
+        q, k, v, do = (rng.standard_normal((n, d)) for _ in range(4))
+        tq, tk, tv = (torch.tensor(a, requires_grad=True) for a in (q, k, v))
+        s = scale * tq @ tk.T
+        if causal:
+            s = s.masked_fill(torch.triu(torch.ones(n, n, dtype=torch.bool), 1), float("-inf"))
+        o = torch.softmax(s, dim=1) @ tv
+        o.backward(torch.tensor(do))
+        dq, dk, dv = impl_bwd(q, k, v, do, scale, causal)
+        for mine, ref in ((dq, tq.grad), (dk, tk.grad), (dv, tv.grad)):
+            assert np.allclose(mine, ref.numpy(), rtol=0, atol=1e-10)
+
+
+def pin_bwd_identities(impl_bwd):
+    """Sums fixed by the softmax: rows of P sum to 1 and rows of dS to 0, so
+    sum_j dV_j = sum_i dO_i and sum_j dK_j = 0; causal row 0 sees one key,
+    so dQ_0 = 0 and the last key only feeds the last query."""
+    rng = np.random.default_rng(23)
+    n, d = 12, 6
+    q, k, v, do = (rng.standard_normal((n, d)) for _ in range(4))
+    for causal in (False, True):
+        dq, dk, dv = impl_bwd(q, k, v, do, 0.6, causal)
+        assert np.allclose(dv.sum(axis=0), do.sum(axis=0), rtol=0, atol=1e-12)
+        assert np.allclose(dk.sum(axis=0), 0.0, rtol=0, atol=1e-12)
+        if causal:
+            assert np.allclose(dq[0], 0.0, rtol=0, atol=1e-14)
+            # key n-1 is seen only by query n-1, with probability P[n-1, n-1]
+            s_last = 0.6 * q[-1] @ k.T
+            p_last = np.exp(s_last - s_last.max())
+            p_last /= p_last.sum()
+            assert np.allclose(dv[-1], p_last[-1] * do[-1], rtol=0, atol=1e-12)
+    zero = impl_bwd(q, k, v, np.zeros_like(do), 0.6, True)
+    assert all(np.array_equal(g, np.zeros_like(g)) for g in zero)
+
+
+BACKWARD_PINS = (pin_bwd_identities, pin_bwd_torch_autograd, pin_bwd_finite_differences)

@@ -38,12 +38,12 @@ MUTANTS = {
 }
 
 
-def _mutant(old, new):
+def _mutant(old, new, name="attention_slice"):
     src = open(ORACLE_SRC).read()
     assert src.count(old) >= 1, f"mutation site {old!r} not found: update MUTANTS"
     mod = types.ModuleType("oracle_mutant")
     exec(compile(src.replace(old, new), "oracle_mutant", "exec"), mod.__dict__)
-    return mod.attention_slice
+    return getattr(mod, name)
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
@@ -58,6 +58,73 @@ def test_pins_catch_planted_mistake(name):
             caught.append((pin.__name__, type(e).__name__))
             break
     assert caught, f"mutant '{name}' passed every pin"
+
+
+@pytest.mark.parametrize("pin", pins.VARLEN_PINS, ids=lambda f: f.__name__)
+def test_varlen_oracle_passes_pin(pin):
+    pin(oracle.attention_varlen)
+
+
+VARLEN_MUTANTS = {
+    "sequence end one row late": ("r0, r1 = cu[b], cu[b + 1]", "r0, r1 = cu[b], cu[b + 1] + 1"),
+    "sequences all start at row 0": ("r0, r1 = cu[b], cu[b + 1]", "r0, r1 = 0, cu[b + 1]"),
+    "queries of head 0 for every head": ("attention_slice(q[r0:r1, h]", "attention_slice(q[r0:r1, 0]"),
+    "last sequence skipped": ("range(len(cu) - 1)", "range(len(cu) - 2)"),
+    "values of the wrong head": ("v[r0:r1, h], scale", "v[r0:r1, H - 1 - h], scale"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(VARLEN_MUTANTS))
+def test_varlen_pins_catch_planted_mistake(name):
+    impl = _mutant(*VARLEN_MUTANTS[name], name="attention_varlen")
+    caught = False
+    for pin in pins.VARLEN_PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin(impl)
+        except Exception:  # an assertion or a crash both count as caught
+            caught = True
+            break
+    assert caught, f"mutant '{name}' passed every varlen pin"
+
+
+BWD_SRC = os.path.join(os.path.dirname(os.path.dirname(__file__)), "oracle", "backward.py")
+
+
+@pytest.mark.parametrize("pin", pins.BACKWARD_PINS, ids=lambda f: f.__name__)
+def test_backward_oracle_passes_pin(pin):
+    pin(oracle.attention_backward_slice)
+
+
+BACKWARD_MUTANTS = {
+    "dQ scale dropped": ("dq = np.float64(scale) * (ds @ k)", "dq = (ds @ k)"),
+    "dK from dS instead of dS^T": ("dk = np.float64(scale) * (ds.T @ q)", "dk = np.float64(scale) * (ds @ q)"),
+    "row term dropped": ("ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))", "ds = p * dp"),
+    "row term over columns": ("(p * dp).sum(axis=1, keepdims=True)", "(p * dp).sum(axis=0, keepdims=True)"),
+    "dV from P instead of P^T": ("dv = p.T @ do", "dv = p @ do"),
+    "dP with V for dO": ("dp = do @ v.T", "dp = v @ do.T"),
+    "P not normalised": ("p[seen] /= l[seen][:, None]", "pass"),
+    "diagonal masked": ("> np.arange(n_q)[:, None]", ">= np.arange(n_q)[:, None]"),
+    "dQ from K^T": ("dq = np.float64(scale) * (ds @ k)", "dq = np.float64(scale) * (ds.T @ k)"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(BACKWARD_MUTANTS))
+def test_backward_pins_catch_planted_mistake(name):
+    old, new = BACKWARD_MUTANTS[name]
+    src = open(BWD_SRC).read()
+    assert src.count(old) >= 1, f"mutation site {old!r} not found"
+    mod = types.ModuleType("oracle_bwd_mutant")
+    exec(compile(src.replace(old, new), "oracle_bwd_mutant", "exec"), mod.__dict__)
+    caught = False
+    for pin in pins.BACKWARD_PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin(mod.attention_backward_slice)
+        except Exception:  # an assertion or a crash both count as caught
+            caught = True
+            break
+    assert caught, f"mutant '{name}' passed every backward pin"
 
 
 def test_e4m3_decode_matches_torch_for_all_codes():
