@@ -34,7 +34,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "fp8": 5000.0}  # MI355X dense matrix-core peaks
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_f16_b8h32n1024d64_traffic.json")
-KERNEL_SOURCES = [os.path.join(ROOT, "io_aware_attention_fwd_amd", "csrc", f) for f in ("fa_fwd.hip", "fa_launch.h")]
+KERNEL_SOURCES = [os.path.join(ROOT, "io_aware_attention_fwd_amd", "csrc", f) for f in ("fa_fwd.hip", "fa_device.h", "fa_launch.h")]
 
 
 def flops(B, H, N, d, causal):
@@ -53,6 +53,11 @@ def kernel_source_hash():
         with open(p, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def progress(msg):
+    """One line per stage on stderr (the JSON result is the only stdout line)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
 def time_calls(fn, warmup, steps, stream):
@@ -163,6 +168,76 @@ def make_call(B, H, N, d, dtype, causal, scale, seed=0, x=None):
     return call, stream, (x, q, k, v, o, lse)
 
 
+def make_call_varlen(lengths, H, d, dtype, causal, scale, seed=0):
+    """fa_fwd_varlen on packed [total, H, d] sequences of the given lengths."""
+    import torch
+
+    from io_aware_attention_fwd_amd import _lib, gen
+
+    x, cu = gen.make_packed(lengths, H, d, dtype, seed=seed)
+    tdt = {"f16": torch.float16, "bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn}[dtype]
+
+    def dev(a):
+        if dtype == "bf16":
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        if dtype == "fp8":
+            return torch.from_numpy(a).view(torch.float8_e4m3fn).cuda()
+        return torch.from_numpy(a).cuda()
+
+    q, k, v = dev(x.q), dev(x.k), dev(x.v)
+    total = q.shape[0]
+    o = torch.empty((total, H, d), dtype=torch.bfloat16 if dtype == "fp8" else tdt, device="cuda")
+    lse = torch.empty((H, total), dtype=torch.float32, device="cuda")
+    cu_t = torch.from_numpy(cu).cuda()
+    stream = torch.cuda.current_stream()
+    s = stream.cuda_stream
+    dt = {"f16": _lib.FA_DTYPE_F16, "bf16": _lib.FA_DTYPE_BF16, "fp8": _lib.FA_DTYPE_FP8_E4M3}[dtype]
+    eff = scale * (x.descale["q"] * x.descale["k"] if dtype == "fp8" else 1.0)
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), cu_t.data_ptr(), len(lengths), H,
+            total, max(lengths), d, eff, int(causal), dt, s)
+    lib = _lib.load()
+
+    def call():
+        rc = lib.fa_fwd_varlen(*args)
+        if rc:
+            raise _lib.FaError(rc, "fa_fwd_varlen")
+    return call, stream, (x, cu, q, k, v, o, lse, cu_t)
+
+
+def cpu_baseline_varlen(x, cu, causal, scale, budget_s):
+    """The float64 oracle on (sequence, head) slices of a packed batch for about
+    ``budget_s`` seconds, extrapolated to the whole batch by FLOPs."""
+    import oracle
+
+    H, d = x.q.shape[1], x.q.shape[2]
+    try:
+        from threadpoolctl import threadpool_info
+
+        cores = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        cores = None
+    lengths = np.diff(cu)
+    total_fl = sum(flops(1, H, int(n), d, causal) for n in lengths)
+    done_fl, n_slices, t0 = 0.0, 0, time.perf_counter()
+    for b in range(len(lengths)):
+        r0, r1 = int(cu[b]), int(cu[b + 1])
+        for h in range(H):
+            qkv = [oracle.dequantize(a[r0:r1, h], x.dtype, x.descale[n]) for a, n in ((x.q, "q"), (x.k, "k"), (x.v, "v"))]
+            oracle.attention_slice(qkv[0], qkv[1], qkv[2], scale, causal)
+            done_fl += flops(1, 1, r1 - r0, d, causal)
+            n_slices += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    el = time.perf_counter() - t0
+    rate = done_fl / el
+    return {"value": rate / 1e12, "unit": "TFLOPS", "cores": cores, "kind": "oracle",
+            "sample": f"{n_slices} (sequence, head) slices of the packed batch ({done_fl / 1e9:.1f} GFLOP, "
+                      f"{x.dtype} inputs, float64 math) timed in {el:.1f} s; whole batch extrapolated by FLOPs to "
+                      f"{total_fl / rate:.1f} s"}
+
+
 def cpu_baseline(x, causal, scale, budget_s):
     """The float64 oracle on as many (b, h) slices of ``x`` as fit in ``budget_s`` seconds."""
     import oracle
@@ -214,6 +289,12 @@ def main(argv=None):
     ap.add_argument("--shape", default=None,
                     help="B,H,N,d,dtype,causal to time another shape instead of the headline one "
                          "(e.g. 2,16,16384,128,bf16,1); the JSON line then names that workload")
+    ap.add_argument("--varlen", default=None,
+                    help="COUNT,LO,HI,H,d,dtype,causal: time fa_fwd_varlen on COUNT packed sequences with lengths "
+                         "drawn uniformly from [LO, HI] (seed 0) instead of the headline shape")
+    ap.add_argument("--bwd", default=None,
+                    help="B,H,N,d,dtype,causal: time the backward pass fa_bwd (after one forward call that "
+                         "produces O and lse) instead of the headline shape")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="also run one device copy of this many MiB (reference kernel for HBM counters)")
     args = ap.parse_args(argv)
@@ -229,11 +310,17 @@ def main(argv=None):
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
 
+    if args.varlen:
+        return main_varlen(args)
+    if args.bwd:
+        return main_bwd(args)
+
     B, H, N, d, dtype, causal = 8, 32, 1024, 64, "f16", False
     if args.shape:
         f = args.shape.split(",")
         B, H, N, d, dtype, causal = int(f[0]), int(f[1]), int(f[2]), int(f[3]), f[4], f[5] in ("1", "true", "True")
     scale = 1.0 / math.sqrt(d)
+    progress(f"inputs B={B} H={H} N={N} d={d} {dtype} causal={int(causal)}")
     call, stream, keep = make_call(B, H, N, d, dtype, causal, scale)
     if args.copy_calib_mib:
         n = args.copy_calib_mib * 2 ** 20 // 4
@@ -259,6 +346,7 @@ def main(argv=None):
                    (8192, 128, "bf16", False), (8192, 128, "bf16", True)]
         inputs = {}
         for n, dd, dt, cz in points:
+            progress(f"sweep point N={n} d={dd} {dt} causal={int(cz)}")
             if (n, dd, dt) not in inputs:  # causal and non-causal points share one input draw
                 inputs = {(n, dd, dt): None}
             c2, st2, keep2 = make_call(B, H, n, dd, dt, cz, 1.0 / math.sqrt(dd), x=inputs[(n, dd, dt)])
@@ -309,8 +397,102 @@ def main(argv=None):
         "gpu_clocks_under_load": clocks,
     }
     if not args.no_cpu:
+        progress("cpu baseline (oracle)")
         line["cpu_baseline"] = cpu_baseline(keep[0], causal, scale, args.cpu_budget)
     print(json.dumps(line), flush=True)
+    return 0
+
+
+def main_bwd(args):
+    """The backward pass on one dense shape: FLOPs counted as the five products
+    of the method (10*B*H*N^2*d, halved for causal)."""
+    import torch
+
+    from io_aware_attention_fwd_amd import _lib, gen
+
+    f = args.bwd.split(",")
+    B, H, N, d, dtype, causal = int(f[0]), int(f[1]), int(f[2]), int(f[3]), f[4], f[5] in ("1", "true")
+    scale = 1.0 / math.sqrt(d)
+    progress(f"backward inputs B={B} H={H} N={N} d={d} {dtype} causal={int(causal)}")
+    call_f, stream, keep = make_call(B, H, N, d, dtype, causal, scale)
+    _, q, k, v, o, lse = keep
+    call_f()
+    do = make_call(B, H, N, d, dtype, causal, scale, seed=100)[2][1]  # dO: a seeded N(0,1) draw of the same shape
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    delta = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    dt = {"f16": _lib.FA_DTYPE_F16, "bf16": _lib.FA_DTYPE_BF16}[dtype]
+    lib = _lib.load()
+    a = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(), dq.data_ptr(),
+         dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), B, H, N, d, scale, int(causal), dt, stream.cuda_stream)
+
+    def call():
+        rc = lib.fa_bwd(*a)
+        if rc:
+            raise _lib.FaError(rc, "fa_bwd")
+    ms = time_calls(call, args.warmup, args.steps, stream)
+    fl = 2.5 * flops(B, H, N, d, causal)
+    peak = PEAK_TFLOPS[dtype]
+    per_call = summarize(time_each(call, 2, min(args.steps, 50), stream), fl, peak)
+    tflops = fl / (ms * 1e-3) / 1e12
+    line = {
+        "metric": "attention fwd TFLOPS + ms at B=8,H=32,d=64,N=512..8192; % of MFMA peak",
+        "value": round(tflops, 2), "unit": "TFLOPS", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5), "per_call": per_call, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": dtype,
+        "data": f"synthetic: i.i.d. N(0,1) Q, K, V (seed 0) and dO (seed 100), stored as {dtype}",
+        "config": {"workload": f"attention backward (dQ, dK, dV) B={B} H={H} N={N} d={d} {dtype} "
+                               f"{'causal' if causal else 'non-causal'} scale=1/sqrt({d})",
+                   "B": B, "H": H, "N": N, "d": d, "causal": causal,
+                   "flop_count": "10*B*H*N^2*d (five products), halved for causal"},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(tflops / peak, 4), "traffic": None},
+        "timing": "HIP events on the kernels' stream; value = K back-to-back calls / elapsed",
+    }
+    print(json.dumps(line), flush=True)
+    del torch
+    return 0
+
+
+def main_varlen(args):
+    """The packed variable-length entry point on a seeded length mix."""
+    import torch
+
+    from io_aware_attention_fwd_amd import gen
+
+    f = args.varlen.split(",")
+    count, lo, hi, H, d, dtype, causal = int(f[0]), int(f[1]), int(f[2]), int(f[3]), int(f[4]), f[5], f[6] in ("1", "true")
+    lengths = gen.length_mix(count, lo, hi, seed=0)
+    scale = 1.0 / math.sqrt(d)
+    progress(f"packed inputs: {count} sequences in [{lo}, {hi}], H={H} d={d} {dtype} causal={int(causal)}")
+    call, stream, keep = make_call_varlen(lengths, H, d, dtype, causal, scale)
+    ms = time_calls(call, args.warmup, args.steps, stream)
+    fl = sum(flops(1, H, n, d, causal) for n in lengths)
+    peak = PEAK_TFLOPS[dtype]
+    per_call = summarize(time_each(call, 2, min(args.steps, 50), stream), fl, peak)
+    tflops = fl / (ms * 1e-3) / 1e12
+    total = sum(lengths)
+    algo_bytes = (3 * (1 if dtype == "fp8" else 2) + 2) * total * H * d + 4 * total * H
+    line = {
+        "metric": "attention fwd TFLOPS + ms at B=8,H=32,d=64,N=512..8192; % of MFMA peak",
+        "value": round(tflops, 2), "unit": "TFLOPS", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5), "per_call": per_call, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": dtype,
+        "data": f"synthetic: i.i.d. N(0,1) inputs from seed 0, stored as {dtype}; lengths from seed 0",
+        "config": {"workload": f"packed variable-length attention forward: {count} sequences, lengths uniform in "
+                               f"[{lo}, {hi}] (total {total} rows), H={H} d={d} {dtype} "
+                               f"{'causal' if causal else 'non-causal'} scale=1/sqrt({d})",
+                   "lengths": lengths, "H": H, "d": d, "causal": causal},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(tflops / peak, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": algo_bytes,
+                     "algorithmic_hbm_gbs": round(algo_bytes / (ms * 1e-3) / 1e9, 1)},
+        "timing": "HIP events on the kernel's stream; value = K back-to-back calls / elapsed",
+    }
+    if not args.no_cpu:
+        progress("cpu baseline (oracle)")
+        line["cpu_baseline"] = cpu_baseline_varlen(keep[0], keep[1], causal, scale, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+    del torch
     return 0
 
 

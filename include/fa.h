@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define FA_VERSION 100 /* major * 10000 + minor * 100 + patch: 0.1.0 */
+#define FA_VERSION 200 /* major * 10000 + minor * 100 + patch: 0.2.0 */
 
 /* Storage format of q, k, v. */
 typedef enum {
@@ -55,12 +55,12 @@ typedef enum {
 /* Return codes. */
 enum {
   FA_OK = 0,
-  FA_ERR_NULL_PTR = -1, /* q, k, v, o or lse is NULL */
-  FA_ERR_SHAPE = -2,    /* B, H or N < 1, a slice of 2 GiB or more, or too many tiles */
+  FA_ERR_NULL_PTR = -1, /* a required pointer (q, k, v, o, lse, cu_seqlens, dout, dq, dk, dv, delta) is NULL */
+  FA_ERR_SHAPE = -2,    /* B, H or N (max_seqlen) < 1, total < 0, a slice of 2 GiB or more, or too many tiles */
   FA_ERR_HEADDIM = -3,  /* d is not 64 or 128 */
-  FA_ERR_DTYPE = -4,    /* dtype is not an fa_dtype value */
+  FA_ERR_DTYPE = -4,    /* dtype is not an fa_dtype value (or is FP8_E4M3 for fa_bwd) */
   FA_ERR_SCALE = -5,    /* scale or a descale is NaN or infinite */
-  FA_ERR_ALIGN = -6,    /* q, k, v or o not 16-byte aligned, or lse not 4-byte aligned */
+  FA_ERR_ALIGN = -6,    /* q, k, v or o not 16-byte aligned, or lse / cu_seqlens not 4-byte aligned */
   FA_ERR_ALIAS = -7,    /* o or lse overlaps an input, or o overlaps lse */
   FA_ERR_HIP = -8       /* the kernel launch reported a HIP error */
 };
@@ -98,6 +98,59 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
                int B, int H, int N, int d, float scale, int causal,
                float q_descale, float k_descale, float v_descale, void* stream);
+
+/*
+ * fa_fwd_varlen -- the same operation for B sequences of different lengths,
+ * packed back to back without padding.  (The pages meet unaligned sequence
+ * lengths by padding them -- page "从RTX 3090到H100：FlashAttention在NVIDIA各代
+ * GPU架构上的性能全景分析", section 3.2, common pitfalls item 2 -- and list
+ * better dynamic-shape support as a direction -- page "FlashAttention与
+ * TensorRT 10集成", section "推理优化的未来方向" item 1; packing instead of
+ * padding is this library's reading.)  Each sequence b is an independent
+ * attention problem over its own rows; causal masking is within a sequence.
+ *
+ *   q, k, v     packed inputs [total, H, d], `dtype` elements: row t of head h
+ *               at element offset (t*H + h)*d.
+ *   o           output [total, H, d], binary16 for F16, bfloat16 otherwise.
+ *   lse         output [H, total] float32 (row t of head h at h*total + t).
+ *   cu_seqlens  device int32 array of B+1 offsets: sequence b owns rows
+ *               cu_seqlens[b] .. cu_seqlens[b+1]-1.  Expected non-decreasing
+ *               from 0 to total.  It is read on the device, not checked on
+ *               the host: a pair that is negative, decreasing, past total or
+ *               longer than max_seqlen makes that sequence empty (its rows are
+ *               not written); no access leaves the buffers.
+ *   B           number of sequences, >= 1 (empty sequences are allowed).
+ *   H, d        heads, head dimension (64 or 128).
+ *   total       rows of the packed tensors, >= 0 (0 enqueues nothing).
+ *   max_seqlen  an upper bound of every sequence length, >= 1; sizes the grid.
+ *   scale, causal, dtype, stream  as for fa_fwd (FP8_E4M3 with descales 1).
+ */
+int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                  const int* cu_seqlens, int B, int H, int total, int max_seqlen,
+                  int d, float scale, int causal, int dtype, void* stream);
+
+/*
+ * fa_bwd -- gradients of fa_fwd: given the output gradient dO, write dQ, dK
+ * and dV.  The probabilities are recomputed from q, k and the saved lse rather
+ * than stored, which is what the "0 MB (重计算)" attention row of the Flash
+ * Attention 2 memory table on page "Optimization Flash Attention 基准测试"
+ * relies on; the formulas are the derivative of the forward definition:
+ *   P = softmax(scale * Q K^T + mask),  dV = P^T dO,  dP = dO V^T,
+ *   dS = P * (dP - rowsum(dO * O)),  dQ = scale * dS K,  dK = scale * dS^T Q.
+ *
+ *   q, k, v, o  the forward inputs and output, [B, H, N, d], F16 or BF16.
+ *   lse         the forward lse, [B, H, N] float32.
+ *   dout        dO, [B, H, N, d], same dtype.
+ *   dq, dk, dv  outputs, [B, H, N, d], same dtype (rounded from float32).
+ *   delta       workspace [B, H, N] float32, overwritten with rowsum(dO * O).
+ *   B, H, N, d, scale, causal, stream  as for fa_fwd; dtype F16 or BF16
+ *               (FP8_E4M3 returns FA_ERR_DTYPE).
+ * Outputs and the workspace must not overlap any input or each other.  Two
+ * kernels are enqueued on `stream` in order.
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+           const void* dout, void* dq, void* dk, void* dv, float* delta,
+           int B, int H, int N, int d, float scale, int causal, int dtype, void* stream);
 
 /* Static description of a return code; never NULL. */
 const char* fa_strerror(int code);

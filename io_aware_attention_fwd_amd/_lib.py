@@ -1,10 +1,11 @@
 """ctypes binding of libfa.so: argument marshalling only.
 
-``fa_fwd``, ``fa_fwd_fp8``, ``fa_strerror`` and ``fa_version`` take the same
-arguments as the C functions declared in ``include/fa.h`` (device pointers as
-Python ints, the stream as a ``hipStream_t`` int or None).  ``fwd`` allocates
-O and lse with torch on the inputs' device and calls ``fa_fwd`` /
-``fa_fwd_fp8`` on torch's current stream.  Every step of the computation runs
+``fa_fwd``, ``fa_fwd_fp8``, ``fa_fwd_varlen``, ``fa_bwd``, ``fa_strerror``
+and ``fa_version`` take the same arguments as the C functions declared in
+``include/fa.h`` (device pointers as Python ints, the stream as a
+``hipStream_t`` int or None).  ``fwd``, ``fwd_varlen`` and ``bwd`` allocate
+their outputs (and the backward workspace) with torch on the inputs' device
+and call the library on torch's current stream.  Every step of the computation runs
 in the library's HIP kernels; if the library is missing or fails to load, the
 call raises.
 """
@@ -49,6 +50,10 @@ def load() -> ctypes.CDLL:
     lib.fa_fwd.restype = ci
     lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, cf, ci, cf, cf, cf, vp]
     lib.fa_fwd_fp8.restype = ci
+    lib.fa_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, cf, ci, ci, vp]
+    lib.fa_fwd_varlen.restype = ci
+    lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, cf, ci, ci, vp]
+    lib.fa_bwd.restype = ci
     lib.fa_strerror.argtypes = [ci]
     lib.fa_strerror.restype = ctypes.c_char_p
     lib.fa_version.argtypes = []
@@ -63,6 +68,15 @@ def fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, stream) -> int:
 
 def fa_fwd_fp8(q, k, v, o, lse, B, H, N, d, scale, causal, q_descale, k_descale, v_descale, stream) -> int:
     return load().fa_fwd_fp8(q, k, v, o, lse, B, H, N, d, scale, int(causal), q_descale, k_descale, v_descale, stream)
+
+
+def fa_fwd_varlen(q, k, v, o, lse, cu_seqlens, B, H, total, max_seqlen, d, scale, causal, dtype, stream) -> int:
+    return load().fa_fwd_varlen(q, k, v, o, lse, cu_seqlens, B, H, total, max_seqlen, d, scale, int(causal), dtype,
+                                stream)
+
+
+def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, scale, causal, dtype, stream) -> int:
+    return load().fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, scale, int(causal), dtype, stream)
 
 
 def fa_strerror(code: int) -> str:
@@ -113,3 +127,65 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: float, causal:
     if rc != 0:
         raise FaError(rc)
     return out, lse
+
+
+def fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor, max_seqlen: int,
+               scale: float, causal: bool = False, *, out: torch.Tensor | None = None,
+               lse: torch.Tensor | None = None, stream: torch.cuda.Stream | None = None):
+    """Attention forward on packed [total, H, d] sequences; returns (O [total, H, d], lse [H, total]).
+
+    ``cu_seqlens`` is an int32 device tensor of B+1 row offsets.  fp8 inputs
+    (``torch.float8_e4m3fn`` or uint8 codes) are taken with descales of 1.
+    """
+    if q.dtype == torch.uint8:
+        q, k, v = (t.view(torch.float8_e4m3fn) for t in (q, k, v))
+    if q.dtype not in _TORCH_DTYPES or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError(f"unsupported dtypes {q.dtype}, {k.dtype}, {v.dtype}")
+    if q.dim() != 3 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError(f"q, k, v must share one [total, H, d] shape, got {tuple(q.shape)}, {tuple(k.shape)}, {tuple(v.shape)}")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k, v must be contiguous")
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or not cu_seqlens.is_contiguous():
+        raise TypeError("cu_seqlens must be a contiguous 1-D int32 tensor")
+    total, H, d = q.shape
+    B = cu_seqlens.numel() - 1
+    dt = _TORCH_DTYPES[q.dtype]
+    o_dtype = torch.bfloat16 if dt == FA_DTYPE_FP8_E4M3 else q.dtype
+    if out is None:
+        out = torch.empty((total, H, d), dtype=o_dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((H, total), dtype=torch.float32, device=q.device)
+    if out.dtype != o_dtype or lse.dtype != torch.float32:
+        raise TypeError("out/lse dtype mismatch")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    rc = fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), cu_seqlens.data_ptr(),
+                       B, H, total, int(max_seqlen), d, float(scale), causal, dt, stream.cuda_stream)
+    if rc != 0:
+        raise FaError(rc, "fa_fwd_varlen")
+    return out, lse
+
+
+def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse: torch.Tensor, dout: torch.Tensor,
+        scale: float, causal: bool = False, *, stream: torch.cuda.Stream | None = None):
+    """Gradients of ``fwd`` on [B, H, N, d] f16/bf16 device tensors; returns (dQ, dK, dV)."""
+    if q.dtype not in (torch.float16, torch.bfloat16):
+        raise TypeError(f"the backward pass takes float16 or bfloat16, got {q.dtype}")
+    for t in (k, v, o, dout):
+        if t.dtype != q.dtype or t.shape != q.shape or not t.is_contiguous():
+            raise ValueError("q, k, v, o, dout must share one contiguous [B, H, N, d] shape and dtype")
+    if q.dim() != 4 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [B, H, N, d] tensor")
+    B, H, N, d = q.shape
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    rc = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(), dq.data_ptr(),
+                dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), B, H, N, d, float(scale), causal, _TORCH_DTYPES[q.dtype],
+                stream.cuda_stream)
+    if rc != 0:
+        raise FaError(rc, "fa_bwd")
+    return dq, dk, dv

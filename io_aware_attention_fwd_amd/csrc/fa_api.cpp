@@ -24,27 +24,38 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
 
 int elem_bytes(fa::Dtype dt) { return dt == fa::Dtype::FP8 ? 1 : 2; }
 
-int forward(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
-            float scale, int causal, fa::Dtype dt, float q_descale, float k_descale, float v_descale,
-            void* stream) {
+// Shape of one call: dense [B,H,N,d] (cu == nullptr) or packed [total,H,d]
+// sequences delimited by cu (N = the longest sequence).
+struct Layout {
+  const int* cu;
+  int B, H, N, total, d;
+};
+
+int forward(const void* q, const void* k, const void* v, void* o, float* lse, const Layout& L, float scale, int causal,
+            fa::Dtype dt, float q_descale, float k_descale, float v_descale, void* stream) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL_PTR;
-  if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
+  const bool packed = L.cu != nullptr;
+  if (L.B < 1 || L.H < 1 || L.N < 1 || (packed && L.total < 0)) return FA_ERR_SHAPE;
+  const int d = L.d;
   if (d != 64 && d != 128) return FA_ERR_HEADDIM;
   if (!isfinite(scale) || !isfinite(q_descale) || !isfinite(k_descale) || !isfinite(v_descale)) return FA_ERR_SCALE;
   const int eb = elem_bytes(dt);
-  const int br = fa::rows_per_workgroup(dt, d, causal != 0, N);
-  // One (batch, head) slice, plus the padding rows of its last tile, must be
-  // addressable with 32-bit byte offsets (the kernels use buffer loads).
-  const int64_t slice_bytes = (int64_t)(N + br) * d * eb;
-  if (slice_bytes >= ((int64_t)1 << 31)) return FA_ERR_SHAPE;
-  const int64_t n_qtiles = ((int64_t)N + br - 1) / br;
-  const int64_t total_wg = n_qtiles * B * H;
+  const int ob = 2;  // O is binary16 / bfloat16 (bfloat16 for fp8 inputs)
+  const int br = fa::rows_per_workgroup(dt, d, causal != 0, L.N);
+  // The rows of one (sequence, head), plus the padding rows of its last tile,
+  // must be addressable with 32-bit byte offsets (the kernels use buffer loads).
+  const int64_t in_row = packed ? (int64_t)L.H * d * eb : (int64_t)d * eb;
+  if ((int64_t)(L.N + br) * in_row >= ((int64_t)1 << 31)) return FA_ERR_SHAPE;
+  const int64_t n_qtiles = ((int64_t)L.N + br - 1) / br;
+  const int64_t total_wg = n_qtiles * L.B * L.H;
   if (total_wg >= ((int64_t)1 << 31)) return FA_ERR_SHAPE;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4) ||
+      (packed && !aligned(L.cu, 4)))
     return FA_ERR_ALIGN;
-  const size_t in_bytes = (size_t)B * H * N * d * eb;
-  const size_t o_bytes = (size_t)B * H * N * d * (dt == fa::Dtype::FP8 ? 2 : eb);
-  const size_t lse_bytes = (size_t)B * H * N * sizeof(float);
+  const int64_t rows = packed ? (int64_t)L.total : (int64_t)L.B * L.N;  // rows per head
+  const size_t in_bytes = (size_t)rows * L.H * d * eb;
+  const size_t o_bytes = (size_t)rows * L.H * d * ob;
+  const size_t lse_bytes = (size_t)rows * L.H * sizeof(float);
   for (const void* in : {q, k, v}) {
     if (overlap(o, o_bytes, in, in_bytes) || overlap(lse, lse_bytes, in, in_bytes)) return FA_ERR_ALIAS;
   }
@@ -59,11 +70,32 @@ int forward(const void* q, const void* k, const void* v, void* o, float* lse, in
   p.v = v;
   p.o = o;
   p.lse = lse;
-  p.B = B;
-  p.H = H;
-  p.N = N;
+  p.cu = L.cu;
+  p.B = L.B;
+  p.H = L.H;
+  p.N = L.N;
+  p.total = packed ? L.total : 0;
   p.n_qtiles = (int)n_qtiles;
   p.total_wg = (int)total_wg;
+  if (packed) {
+    p.in_batch = 0;
+    p.in_head = (long long)d * eb;
+    p.in_row = (int)in_row;
+    p.out_batch = 0;
+    p.out_head = (long long)d * ob;
+    p.out_row = L.H * d * ob;
+    p.lse_batch = 0;
+    p.lse_head = L.total;
+  } else {
+    p.in_row = d * eb;
+    p.in_head = (long long)L.N * p.in_row;
+    p.in_batch = (long long)L.H * p.in_head;
+    p.out_row = d * ob;
+    p.out_head = (long long)L.N * p.out_row;
+    p.out_batch = (long long)L.H * p.out_head;
+    p.lse_head = L.N;
+    p.lse_batch = (long long)L.H * L.N;
+  }
   const uint32_t sign_bits = dt == fa::Dtype::FP8 ? 0x80808080u : 0x80008000u;
   p.q_xor = eff < 0 ? sign_bits : 0u;
   p.q_and = eff == 0 ? 0u : 0xFFFFFFFFu;
@@ -71,9 +103,64 @@ int forward(const void* q, const void* k, const void* v, void* o, float* lse, in
   if (!isfinite(p.c)) return FA_ERR_SCALE;
   p.o_mul = v_descale;
 
+  if (packed && L.total == 0) return FA_OK;  // no rows: nothing to compute
   if (fa::launch_fwd(dt, d, causal != 0, p, static_cast<hipStream_t>(stream)) != hipSuccess) return FA_ERR_HIP;
   return FA_OK;
 }
+
+int backward(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout, void* dq,
+             void* dk, void* dv, float* delta, int B, int H, int N, int d, float scale, int causal, int dtype,
+             void* stream) {
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !delta) return FA_ERR_NULL_PTR;
+  if (dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
+  if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+  if (!isfinite(scale)) return FA_ERR_SCALE;
+  const int64_t row = (int64_t)d * 2;
+  if ((int64_t)(N + fa::kBwdRows) * row >= ((int64_t)1 << 31)) return FA_ERR_SHAPE;
+  const int64_t n_blocks = ((int64_t)N + fa::kBwdRows - 1) / fa::kBwdRows;
+  const int64_t total_wg = n_blocks * B * H;
+  if (total_wg >= ((int64_t)1 << 31)) return FA_ERR_SHAPE;
+  for (const void* ptr : {q, k, v, o, dout, (const void*)dq, (const void*)dk, (const void*)dv})
+    if (!aligned(ptr, 16)) return FA_ERR_ALIGN;
+  if (!aligned(lse, 4) || !aligned(delta, 4)) return FA_ERR_ALIGN;
+  const size_t t_bytes = (size_t)B * H * N * d * 2;
+  const size_t r_bytes = (size_t)B * H * N * sizeof(float);
+  const void* ins[] = {q, k, v, o, lse, dout};
+  const size_t in_sz[] = {t_bytes, t_bytes, t_bytes, t_bytes, r_bytes, t_bytes};
+  void* outs[] = {dq, dk, dv, delta};
+  const size_t out_sz[] = {t_bytes, t_bytes, t_bytes, r_bytes};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 6; ++j)
+      if (overlap(outs[i], out_sz[i], ins[j], in_sz[j])) return FA_ERR_ALIAS;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(outs[i], out_sz[i], outs[j], out_sz[j])) return FA_ERR_ALIAS;
+  }
+  fa::BwdParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.dout = dout;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.delta = delta;
+  p.B = B;
+  p.H = H;
+  p.N = N;
+  p.n_blocks = (int)n_blocks;
+  p.total_wg = (int)total_wg;
+  p.c = (float)((double)scale * (double)kLog2e);
+  p.scale = scale;
+  if (!isfinite(p.c)) return FA_ERR_SCALE;
+  if (fa::launch_bwd(static_cast<fa::Dtype>(dtype), d, causal != 0, p, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return FA_ERR_HIP;
+  return FA_OK;
+}
+
+bool known_dtype(int dtype) { return dtype == FA_DTYPE_F16 || dtype == FA_DTYPE_BF16 || dtype == FA_DTYPE_FP8_E4M3; }
 
 }  // namespace
 
@@ -81,29 +168,47 @@ extern "C" {
 
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d, float scale,
            int causal, int dtype, void* stream) {
-  if (dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_FP8_E4M3) {
+  if (!known_dtype(dtype)) {
     if (!q || !k || !v || !o || !lse) return FA_ERR_NULL_PTR;
     return FA_ERR_DTYPE;
   }
-  return forward(q, k, v, o, lse, B, H, N, d, scale, causal, static_cast<fa::Dtype>(dtype), 1.0f, 1.0f, 1.0f,
-                 stream);
+  return forward(q, k, v, o, lse, Layout{nullptr, B, H, N, 0, d}, scale, causal, static_cast<fa::Dtype>(dtype), 1.0f,
+                 1.0f, 1.0f, stream);
 }
 
 int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
                float scale, int causal, float q_descale, float k_descale, float v_descale, void* stream) {
-  return forward(q, k, v, o, lse, B, H, N, d, scale, causal, fa::Dtype::FP8, q_descale, k_descale, v_descale,
-                 stream);
+  return forward(q, k, v, o, lse, Layout{nullptr, B, H, N, 0, d}, scale, causal, fa::Dtype::FP8, q_descale, k_descale,
+                 v_descale, stream);
+}
+
+int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse, const int* cu_seqlens, int B,
+                  int H, int total, int max_seqlen, int d, float scale, int causal, int dtype, void* stream) {
+  if (!cu_seqlens) return FA_ERR_NULL_PTR;
+  if (!known_dtype(dtype)) {
+    if (!q || !k || !v || !o || !lse) return FA_ERR_NULL_PTR;
+    return FA_ERR_DTYPE;
+  }
+  return forward(q, k, v, o, lse, Layout{cu_seqlens, B, H, max_seqlen, total, d}, scale, causal,
+                 static_cast<fa::Dtype>(dtype), 1.0f, 1.0f, 1.0f, stream);
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout, void* dq,
+           void* dk, void* dv, float* delta, int B, int H, int N, int d, float scale, int causal, int dtype,
+           void* stream) {
+  return backward(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, scale, causal, dtype, stream);
 }
 
 const char* fa_strerror(int code) {
   switch (code) {
     case FA_OK: return "success";
     case FA_ERR_NULL_PTR: return "a required pointer is NULL";
-    case FA_ERR_SHAPE: return "invalid shape: B, H and N must be >= 1 and one slice must stay below 2 GiB";
+    case FA_ERR_SHAPE:
+      return "invalid shape: B, H and N (or max_seqlen) must be >= 1, total >= 0, and one slice must stay below 2 GiB";
     case FA_ERR_HEADDIM: return "unsupported head dimension: d must be 64 or 128";
-    case FA_ERR_DTYPE: return "unknown dtype";
+    case FA_ERR_DTYPE: return "unknown dtype (or fp8 given to the backward pass)";
     case FA_ERR_SCALE: return "scale or descale is not finite";
-    case FA_ERR_ALIGN: return "misaligned pointer: q, k, v, o need 16 bytes, lse 4 bytes";
+    case FA_ERR_ALIGN: return "misaligned pointer: q, k, v, o need 16 bytes, lse and cu_seqlens 4 bytes";
     case FA_ERR_ALIAS: return "an output overlaps an input or the other output";
     case FA_ERR_HIP: return "the kernel launch reported a HIP error";
     default: return "unknown error code";

@@ -1,0 +1,434 @@
+// FlashAttention backward pass for gfx950 (MI355X, CDNA4): dQ, dK, dV from
+// Q, K, V, the forward output O, its logsumexp and the output gradient dO.
+//
+// The probabilities are recomputed from Q, K and the saved logsumexp instead
+// of being read back (the "0 MB (重计算)" attention row of the Flash
+// Attention 2 memory table on page "Optimization Flash Attention 基准测试"):
+//   P = exp(scale*Q K^T - lse) (masked),   dV = P^T dO,   dP = dO V^T,
+//   dS = P * (dP - D) with D_i = sum_c dO_ic O_ic,   dQ = scale * dS K,
+//   dK = scale * dS^T Q.
+//
+// Two kernels on one stream, no atomics:
+//   * dQ kernel: one workgroup per block of 128 queries of one (batch, head)
+//     (4 waves x 32 queries).  It writes D for its queries to the workspace,
+//     streams K/V tiles of 64 keys through LDS and accumulates dQ^T = K^T dS^T
+//     exactly like the forward pass accumulates O^T = V^T P^T: scores are
+//     computed transposed (S^T = K Q^T, dP^T = V dO^T) so every lane owns one
+//     query, dS^T feeds the matrix instruction straight from the accumulators,
+//     and K^T comes from transposing LDS reads.
+//   * dK/dV kernel: one workgroup per block of 128 keys (4 waves x 32 keys),
+//     K and V rows held in registers, query tiles of 32 rows (Q, dO, lse, D)
+//     streamed through LDS.  S = Q K^T and dP = dO V^T give every lane one
+//     key; dV^T += dO^T P and dK^T += Q^T dS take P and dS from the
+//     accumulators and dO^T, Q^T from transposing LDS reads.
+// Masked scores are set to -inf after the scale is applied (the scale may be
+// negative here), so their probabilities are exactly 0.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fa_device.h"
+#include "fa_launch.h"
+
+namespace fa {
+namespace {
+
+constexpr float kLog2e = 1.44269504088896341f;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <int D>
+struct BwdShape {
+  static constexpr int kDB = D / 32;      // 32-wide blocks of the head dimension
+  static constexpr int kSteps = D / 16;   // 16-wide k-steps of a product over d
+  static constexpr int kRow = 2 * D;      // bytes per row (16-bit elements)
+  static constexpr int kCR = kRow / 16;   // 16-byte chunks per row
+  using VL = VLayout<kRow, false>;
+  static constexpr int kGV = VL::kGroupBytes / 16;  // LDS granules per group of rows
+  static constexpr int kRSK = kRow + 16;            // padded row of a tile read by rows only
+};
+
+// sum of the two 16-bit products of a packed pair, accumulated in float32
+template <bool BF16>
+__device__ __forceinline__ float dot_pair(u32 a, u32 b, float acc) {
+  if (BF16) {
+    const float a0 = __builtin_bit_cast(float, a << 16), a1 = __builtin_bit_cast(float, a & 0xFFFF0000u);
+    const float b0 = __builtin_bit_cast(float, b << 16), b1 = __builtin_bit_cast(float, b & 0xFFFF0000u);
+    return __builtin_fmaf(a1, b1, __builtin_fmaf(a0, b0, acc));
+  }
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(fp16x2, a), __builtin_bit_cast(fp16x2, b), acc, false);
+}
+
+// Direct HBM -> LDS load of `rows` rows (from row r0 of the slice) into the
+// grouped, padded layout VL (see fa_device.h); NW waves share the work.
+template <int D, int NW, int ROWS>
+__device__ __forceinline__ void issue_rows_vl(__amdgpu_buffer_rsrc_t rs, char* dst, int r0, int wave, int lane) {
+  using B = BwdShape<D>;
+  constexpr int kGran = ROWS / B::VL::kGroupRows * B::kGV;
+  constexpr int kBlk = (kGran + 63) / 64;
+#pragma unroll
+  for (int j = 0; j < (kBlk + NW - 1) / NW; ++j) {
+    const int blk = wave + j * NW;
+    const int g = blk * 64 + lane;
+    const int grp = g / B::kGV;
+    const int off = (g - grp * B::kGV) * 16;
+    int r = -1, c = 0;
+#pragma unroll
+    for (int i = 0; i < B::VL::kGroupRows; ++i)
+      if (off >= B::VL::row(i) && off < B::VL::row(i) + B::kRow) {
+        r = grp * B::VL::kGroupRows + i;
+        c = (off - B::VL::row(i)) / 16;
+      }
+    if (blk < kBlk && g < kGran && r >= 0) load_lds16(rs, dst + blk * 1024, (r0 + r) * B::kRow + c * 16);
+  }
+}
+
+// The same for a tile read only by rows: one 16-byte pad granule per row.
+template <int D, int NW, int ROWS>
+__device__ __forceinline__ void issue_rows_k(__amdgpu_buffer_rsrc_t rs, char* dst, int r0, int wave, int lane) {
+  using B = BwdShape<D>;
+  constexpr int kG = B::kCR + 1;
+  constexpr int kGran = ROWS * kG;
+  constexpr int kBlk = (kGran + 63) / 64;
+#pragma unroll
+  for (int j = 0; j < (kBlk + NW - 1) / NW; ++j) {
+    const int blk = wave + j * NW;
+    const int g = blk * 64 + lane;
+    const int r = g / kG, c = g - r * kG;
+    if (blk < kBlk && g < kGran && c < B::kCR) load_lds16(rs, dst + blk * 1024, (r0 + r) * B::kRow + c * 16);
+  }
+}
+
+// 128-bit operand of matrix instruction step s for row `row` of a slice,
+// straight from HBM: lane (half, .) gets elements 16*s + 8*half .. +7.
+template <int D>
+__device__ __forceinline__ void load_row_operand(__amdgpu_buffer_rsrc_t rs, int row, int half, u32x4 (&dst)[D / 16]) {
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s)
+    dst[s] = __builtin_amdgcn_raw_buffer_load_b128(rs, row * (2 * D) + (16 * s + 8 * half) * 2, 0, 0);
+}
+
+// Transposing read of a 32-row block (rows 32*kb .. +31) of a VL tile: the A
+// operand (column block db, k-step t) of a product that sums over those rows.
+template <int D>
+__device__ __forceinline__ u32x4 tr_operand(const char* tile, int base, int db, int kb, int t) {
+  using B = BwdShape<D>;
+  const int o = base + B::VL::row(32 * kb + 16 * t) + 64 * db;
+  const u32x2 lo = lds_read_tr16(tile, o);
+  const u32x2 hi = lds_read_tr16(tile, o + B::VL::row(8));
+  return u32x4{lo[0], lo[1], hi[0], hi[1]};
+}
+
+template <int D>
+__device__ __forceinline__ int tr_base(int lane) {
+  using B = BwdShape<D>;
+  const int g = lane >> 4, u = lane & 15, half = lane >> 5;
+  return B::VL::row(4 * half + (u >> 2)) + 2 * (16 * (g & 1) + 4 * (u & 3));
+}
+
+// Store a d x 32 block set of transposed accumulators (lane owns one row of
+// the output: a query for dQ, a key for dK/dV) as 16-bit values times `mul`.
+template <bool BF16, int D>
+__device__ __forceinline__ void store_rowT(char* row_ptr, const f32x16 (&acc)[D / 32], int half, float mul) {
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int a4 = 0; a4 < 4; ++a4) {
+      const int col = 32 * db + 8 * a4 + 4 * half;
+      u32x2 w;
+      w[0] = pack_p<BF16>(acc[db][4 * a4 + 0] * mul, acc[db][4 * a4 + 1] * mul);
+      w[1] = pack_p<BF16>(acc[db][4 * a4 + 2] * mul, acc[db][4 * a4 + 3] * mul);
+      *reinterpret_cast<u32x2*>(row_ptr + col * 2) = w;
+    }
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------- dQ kernel
+template <class Tr, int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(BwdParams p) {
+  constexpr int NW = 4, BC = 64, kKB = 2;
+  constexpr bool kBf = Tr::kPvBf16;
+  using B = BwdShape<D>;
+  constexpr int kSK = BC / B::VL::kGroupRows * B::VL::kGroupBytes;  // K tile, grouped layout
+  constexpr int kSV = BC * B::kRSK;                                  // V tile, padded rows
+  __shared__ __attribute__((aligned(16))) char lds_k0[kSK];
+  __shared__ __attribute__((aligned(16))) char lds_k1[kSK];
+  __shared__ __attribute__((aligned(16))) char lds_v0[kSV];
+  __shared__ __attribute__((aligned(16))) char lds_v1[kSV];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, half = lane >> 5, l32 = lane & 31;
+  const int tile = xcd_remap(blockIdx.x, p.total_wg);
+  const int bh = tile / p.n_blocks;
+  int qt = tile - bh * p.n_blocks;
+  if (CAUSAL) qt = p.n_blocks - 1 - qt;
+  const int N = p.N;
+  const int q0 = qt * kBwdRows, qw0 = q0 + wave * 32, qi = qw0 + l32;
+  const u32 slice = (u32)N * B::kRow;
+  const size_t base = (size_t)bh * N * B::kRow;
+  const auto rq = make_rsrc((const char*)p.q + base, slice);
+  const auto rk = make_rsrc((const char*)p.k + base, slice);
+  const auto rv = make_rsrc((const char*)p.v + base, slice);
+  const auto ro = make_rsrc((const char*)p.o + base, slice);
+  const auto rdo = make_rsrc((const char*)p.dout + base, slice);
+
+  // this lane's query row: Q and dO as matrix operands, D = dO . O, lse
+  u32x4 q16[B::kSteps], do16[B::kSteps], o16[B::kSteps];
+  load_row_operand<D>(rq, qi, half, q16);
+  load_row_operand<D>(rdo, qi, half, do16);
+  load_row_operand<D>(ro, qi, half, o16);
+  float dpart = 0.f;
+#pragma unroll
+  for (int s = 0; s < B::kSteps; ++s)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dpart = dot_pair<kBf>(do16[s][e], o16[s][e], dpart);
+  const float Dq = halves_sum(dpart);
+  const float Lq = qi < N ? p.lse[(size_t)bh * N + qi] * kLog2e : 0.f;
+  if (half == 0 && qi < N) p.delta[(size_t)bh * N + qi] = Dq;
+  const float c = p.c;
+
+  const int n_all = (N + BC - 1) / BC;
+  const int n_kv = CAUSAL ? min(n_all, (q0 + kBwdRows - 1) / BC + 1) : n_all;
+  const bool has_rows = qw0 < N;
+
+  f32x16 dqacc[B::kDB];
+#pragma unroll
+  for (int db = 0; db < B::kDB; ++db) dqacc[db] = f32x16{};
+  const int kbase = B::VL::row(l32) + 16 * half;  // row operand of the K tile (grouped layout)
+  const int vbase = l32 * B::kRSK + 16 * half;    // row operand of the V tile (padded rows)
+  const int tbase = tr_base<D>(lane);
+
+  auto step = [&](int kt, const char* lk, const char* lv) __attribute__((always_inline)) {
+    if (!has_rows || (CAUSAL && kt * BC > qw0 + 31)) return;
+    f32x16 st[kKB], dpt[kKB];
+#pragma unroll
+    for (int kb = 0; kb < kKB; ++kb) {
+      st[kb] = f32x16{};
+      dpt[kb] = f32x16{};
+#pragma unroll
+      for (int s = 0; s < B::kSteps; ++s) {
+        const u32x4 ka = lds_read_b128(lk, kbase + B::VL::row(32 * kb) + 32 * s);
+        st[kb] = mfma16(ka, q16[s], st[kb], kBf);
+        const u32x4 va = lds_read_b128(lv, vbase + 32 * kb * B::kRSK + 32 * s);
+        dpt[kb] = mfma16(va, do16[s], dpt[kb], kBf);
+      }
+    }
+    const int k0 = kt * BC;
+    const int lim = CAUSAL ? min(qi, N - 1) : N - 1;  // last key this query sees
+    const bool need_mask = (k0 + BC > N) || (CAUSAL && k0 + BC - 1 > qw0);
+    u32x4 pb[kKB][2];
+#pragma unroll
+    for (int kb = 0; kb < kKB; ++kb)
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float ds[2];
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const int r = 8 * t + 2 * e + j;
+            float x = __builtin_fmaf(st[kb][r], c, -Lq);
+            if (need_mask) {
+              const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+              if (key > lim) x = -INFINITY;
+            }
+            const float pr = __builtin_amdgcn_exp2f(x);
+            ds[j] = pr * (dpt[kb][r] - Dq);
+          }
+          pb[kb][t][e] = pack_p<kBf>(ds[0], ds[1]);
+        }
+#pragma unroll
+    for (int db = 0; db < B::kDB; ++db)
+#pragma unroll
+      for (int kb = 0; kb < kKB; ++kb)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) dqacc[db] = mfma16(tr_operand<D>(lk, tbase, db, kb, t), pb[kb][t], dqacc[db], kBf);
+  };
+
+  issue_rows_vl<D, NW, BC>(rk, lds_k0, 0, wave, lane);
+  issue_rows_k<D, NW, BC>(rv, lds_v0, 0, wave, lane);
+  for (int kt = 0; kt < n_kv; kt += 2) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (kt + 1 < n_kv) {
+      issue_rows_vl<D, NW, BC>(rk, lds_k1, (kt + 1) * BC, wave, lane);
+      issue_rows_k<D, NW, BC>(rv, lds_v1, (kt + 1) * BC, wave, lane);
+    }
+    step(kt, lds_k0, lds_v0);
+    if (kt + 1 < n_kv) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (kt + 2 < n_kv) {
+        issue_rows_vl<D, NW, BC>(rk, lds_k0, (kt + 2) * BC, wave, lane);
+        issue_rows_k<D, NW, BC>(rv, lds_v0, (kt + 2) * BC, wave, lane);
+      }
+      step(kt + 1, lds_k1, lds_v1);
+    }
+  }
+
+  if (qi < N) store_rowT<kBf, D>((char*)p.dq + base + (size_t)qi * B::kRow, dqacc, half, p.scale);
+}
+
+// ------------------------------------------------------------ dK/dV kernel
+template <class Tr, int D, bool CAUSAL>
+__global__ __launch_bounds__(256, D == 64 ? 2 : 1) void fa_bwd_dkdv_kernel(BwdParams p) {
+  constexpr int NW = 4, BQ = 32;
+  constexpr bool kBf = Tr::kPvBf16;
+  using B = BwdShape<D>;
+  constexpr int kST = BQ / B::VL::kGroupRows * B::VL::kGroupBytes;  // a Q or dO tile, grouped layout
+  __shared__ __attribute__((aligned(16))) char lds_q0[kST];
+  __shared__ __attribute__((aligned(16))) char lds_q1[kST];
+  __shared__ __attribute__((aligned(16))) char lds_d0[kST];
+  __shared__ __attribute__((aligned(16))) char lds_d1[kST];
+  __shared__ __attribute__((aligned(16))) float lds_ld0[2 * BQ];  // lse (natural log) then D of the tile's rows
+  __shared__ __attribute__((aligned(16))) float lds_ld1[2 * BQ];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, half = lane >> 5, l32 = lane & 31;
+  const int tile = xcd_remap(blockIdx.x, p.total_wg);
+  const int bh = tile / p.n_blocks;
+  const int kblk = tile - bh * p.n_blocks;
+  const int N = p.N;
+  const int k0 = kblk * kBwdRows, kw0 = k0 + wave * 32, key = kw0 + l32;
+  const u32 slice = (u32)N * B::kRow;
+  const size_t base = (size_t)bh * N * B::kRow;
+  const auto rq = make_rsrc((const char*)p.q + base, slice);
+  const auto rk = make_rsrc((const char*)p.k + base, slice);
+  const auto rv = make_rsrc((const char*)p.v + base, slice);
+  const auto rdo = make_rsrc((const char*)p.dout + base, slice);
+  const auto rl = make_rsrc(p.lse + (size_t)bh * N, (u32)N * 4);
+  const auto rd = make_rsrc(p.delta + (size_t)bh * N, (u32)N * 4);
+
+  // this lane's key row of K and V as matrix operands
+  u32x4 k16[B::kSteps], v16[B::kSteps];
+  load_row_operand<D>(rk, key, half, k16);
+  load_row_operand<D>(rv, key, half, v16);
+  const float c = p.c;
+
+  f32x16 dkacc[B::kDB], dvacc[B::kDB];
+#pragma unroll
+  for (int db = 0; db < B::kDB; ++db) {
+    dkacc[db] = f32x16{};
+    dvacc[db] = f32x16{};
+  }
+  const int rbase = B::VL::row(l32) + 16 * half;  // row operand of a Q or dO tile
+  const int tbase = tr_base<D>(lane);
+  const int n_qt = (N + BQ - 1) / BQ;
+  const int qt0 = CAUSAL ? k0 / BQ : 0;  // earlier queries see none of this block's keys
+  const bool has_keys = kw0 < N;
+
+  // wave 0 fetches the tile's 32 lse values (lanes 0..7, into dst[0..31]) and
+  // its 32 D values (lanes 8..15, into dst[32..63]): a direct load writes
+  // lane L's 16 bytes at dst + 16*L
+  auto issue_ld = [&](int qt, float* dst) __attribute__((always_inline)) {
+    if (wave == 0) {
+      const int r = qt * BQ + 4 * (lane & 7);
+      if (lane < 8) load_lds16(rl, (char*)dst, r * 4);
+      if (lane >= 8 && lane < 16) load_lds16(rd, (char*)dst, r * 4);
+    }
+  };
+  auto issue = [&](int qt, char* dq_tile, char* ddo_tile, float* dld) __attribute__((always_inline)) {
+    issue_rows_vl<D, NW, BQ>(rq, dq_tile, qt * BQ, wave, lane);
+    issue_rows_vl<D, NW, BQ>(rdo, ddo_tile, qt * BQ, wave, lane);
+    issue_ld(qt, dld);
+  };
+
+  auto step = [&](int qt, const char* tq, const char* tdo, const float* tld) __attribute__((always_inline)) {
+    const int qb0 = qt * BQ;
+    if (!has_keys || (CAUSAL && qb0 + BQ - 1 < kw0)) return;  // no query of the tile sees these keys
+    f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+    for (int st = 0; st < B::kSteps; ++st) {
+      const u32x4 qa = lds_read_b128(tq, rbase + 32 * st);
+      s = mfma16(qa, k16[st], s, kBf);
+      const u32x4 da = lds_read_b128(tdo, rbase + 32 * st);
+      dp = mfma16(da, v16[st], dp, kBf);
+    }
+    // element r of the accumulators belongs to query row 8*(r/4) + 4*half + r%4 of the tile
+    float L[16], Dr[16];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      // (whole-vector casts: a bit cast of a vector element subscript reads
+      // element 0 whatever the index)
+      const f32x4 l4 = __builtin_bit_cast(f32x4, lds_read_b128((const char*)tld, (8 * g + 4 * half) * 4));
+      const f32x4 d4 = __builtin_bit_cast(f32x4, lds_read_b128((const char*)tld, (BQ + 8 * g + 4 * half) * 4));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        L[4 * g + e] = l4[e] * kLog2e;
+        Dr[4 * g + e] = d4[e];
+      }
+    }
+    const bool need_mask = (qb0 + BQ > N) || (CAUSAL && qb0 < kw0 + 31);
+    u32x4 pp[2], pds[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float pr[2], ds[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int r = 8 * t + 2 * e + j;
+          float x = __builtin_fmaf(s[r], c, -L[r]);
+          if (need_mask) {
+            const int query = qb0 + 8 * (r >> 2) + 4 * half + (r & 3);
+            if (query >= N || (CAUSAL && key > query)) x = -INFINITY;
+          }
+          pr[j] = __builtin_amdgcn_exp2f(x);
+          ds[j] = pr[j] * (dp[r] - Dr[r]);
+        }
+        pp[t][e] = pack_p<kBf>(pr[0], pr[1]);
+        pds[t][e] = pack_p<kBf>(ds[0], ds[1]);
+      }
+#pragma unroll
+    for (int db = 0; db < B::kDB; ++db)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        dvacc[db] = mfma16(tr_operand<D>(tdo, tbase, db, 0, t), pp[t], dvacc[db], kBf);
+        dkacc[db] = mfma16(tr_operand<D>(tq, tbase, db, 0, t), pds[t], dkacc[db], kBf);
+      }
+  };
+
+  if (qt0 < n_qt) issue(qt0, lds_q0, lds_d0, lds_ld0);
+  for (int qt = qt0; qt < n_qt; qt += 2) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (qt + 1 < n_qt) issue(qt + 1, lds_q1, lds_d1, lds_ld1);
+    step(qt, lds_q0, lds_d0, lds_ld0);
+    if (qt + 1 < n_qt) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (qt + 2 < n_qt) issue(qt + 2, lds_q0, lds_d0, lds_ld0);
+      step(qt + 1, lds_q1, lds_d1, lds_ld1);
+    }
+  }
+
+  if (key < N) {
+    store_rowT<kBf, D>((char*)p.dk + base + (size_t)key * B::kRow, dkacc, half, p.scale);
+    store_rowT<kBf, D>((char*)p.dv + base + (size_t)key * B::kRow, dvacc, half, 1.f);
+  }
+}
+
+namespace {
+
+template <class Tr, int D, bool CAUSAL>
+hipError_t launch_bwd_typed(const BwdParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL((fa_bwd_dq_kernel<Tr, D, CAUSAL>), dim3(p.total_wg), dim3(256), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<Tr, D, CAUSAL>), dim3(p.total_wg), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <class Tr>
+hipError_t launch_bwd_dtype(int d, bool causal, const BwdParams& p, hipStream_t stream) {
+  if (d == 64) return causal ? launch_bwd_typed<Tr, 64, true>(p, stream) : launch_bwd_typed<Tr, 64, false>(p, stream);
+  return causal ? launch_bwd_typed<Tr, 128, true>(p, stream) : launch_bwd_typed<Tr, 128, false>(p, stream);
+}
+
+}  // namespace
+
+hipError_t launch_bwd(Dtype dt, int d, bool causal, const BwdParams& p, hipStream_t stream) {
+  if (d != 64 && d != 128) return hipErrorInvalidValue;
+  if (dt == Dtype::F16) return launch_bwd_dtype<TrF16>(d, causal, p, stream);
+  if (dt == Dtype::BF16) return launch_bwd_dtype<TrBF16>(d, causal, p, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace fa

@@ -41,200 +41,11 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include "fa_device.h"
 #include "fa_launch.h"
 
 namespace fa {
 namespace {
-
-typedef uint32_t u32;
-typedef u32 u32x4 __attribute__((ext_vector_type(4)));
-typedef u32 u32x2 __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef int i32x2 __attribute__((ext_vector_type(2)));
-typedef int i32x8 __attribute__((ext_vector_type(8)));
-typedef __attribute__((address_space(3))) void lds_void;
-
-constexpr float kLn2 = 0.69314718055994531f;
-constexpr float kRescaleThreshold = 8.0f;  // log2 of the largest probability allowed before rescaling
-constexpr u32 kRsrcWord3 = 0x00020000u;    // raw buffer, 32-bit data format, range-checked
-
-// ---------------------------------------------------------------- dtype traits
-struct TrF16 {
-  static constexpr bool kFp8 = false;
-  static constexpr int kEK = 2;  // bytes per Q/K element
-  static constexpr int kEV = 2;  // bytes per V element
-  static constexpr bool kPvBf16 = false;
-};
-struct TrBF16 {
-  static constexpr bool kFp8 = false;
-  static constexpr int kEK = 2;
-  static constexpr int kEV = 2;
-  static constexpr bool kPvBf16 = true;
-};
-struct TrFP8 {
-  static constexpr bool kFp8 = true;
-  static constexpr int kEK = 1;
-  static constexpr int kEV = 1;
-  static constexpr bool kPvBf16 = true;  // P V in bfloat16 with V widened exactly
-};
-
-__device__ __forceinline__ f32x16 mfma16(u32x4 a, u32x4 b, f32x16 c, bool bf16) {
-  if (bf16)
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
-                                                   0, 0);
-  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
-}
-
-__device__ __forceinline__ f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c) {
-  // operand format code 0 = E4M3 for both; zero scale operands leave them unscaled
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
-}
-
-// Two floats -> one packed 16-bit pair, round to nearest even (one
-// v_cvt_pk_f16_f32 / v_cvt_pk_bf16_f32 on gfx950).
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-template <bool BF16>
-__device__ __forceinline__ u32 pack_p(float lo, float hi) {
-  const f32x2 x = {lo, hi};
-  if (BF16) return __builtin_bit_cast(u32, __builtin_convertvector(x, bf16x2));
-  return __builtin_bit_cast(u32, __builtin_convertvector(x, f16x2));
-}
-
-// Combine lane l with lane l ^ 32 (the other half-wave) without touching LDS
-// (an LDS permute would be ordered behind the operand reads in flight).
-// v_permlane32_swap exchanges the upper half-wave of its first operand with
-// the lower half-wave of its second; applied to two copies of x it leaves the
-// lower half-wave's values in every lane of one and the upper half-wave's in
-// every lane of the other, so a symmetric combination of the two gives each
-// lane the pairwise result.  It is written as inline assembly because the
-// compiler's model of the builtin folds that symmetric combination into a
-// single operand.
-__device__ __forceinline__ void swap_halves(u32& a, u32& b) {
-  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
-}
-__device__ __forceinline__ float halves_max(float x) {
-  u32 a = __builtin_bit_cast(u32, x), b = a;
-  swap_halves(a, b);
-  return __builtin_elementwise_maximum(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
-}
-__device__ __forceinline__ float halves_sum(float x) {
-  u32 a = __builtin_bit_cast(u32, x), b = a;
-  swap_halves(a, b);
-  return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
-}
-
-// acc + p0 + p1 for the row sum.  binary16 sums the rounded pair with one
-// v_dot2c_f32_f16 (rounding moves the sum by at most 2^-11 relative, well
-// inside the lse bar, and matches the values that enter P V).  bfloat16's
-// 2^-8 rounding would be too coarse for lse, so its sum uses the float32
-// values.
-typedef __fp16 fp16x2 __attribute__((ext_vector_type(2)));
-template <bool BF16>
-__device__ __forceinline__ float sum_pair(u32 packed, float p0, float p1, float acc) {
-  if (BF16) return acc + (p0 + p1);
-  const fp16x2 one = {(__fp16)1.0f, (__fp16)1.0f};
-  return __builtin_amdgcn_fdot2(__builtin_bit_cast(fp16x2, packed), one, acc, false);
-}
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, u32 bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, (int)kRsrcWord3);
-}
-
-// 16 bytes per lane from a buffer straight into LDS: lane L of the wave writes
-// lds_block + 16 * L; an out-of-range offset writes zeros.  (Kept in a device
-// function: in a lambda the host pass would see the builtin too.)
-__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rsrc, char* lds_block, int voffset) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)lds_block, 16, voffset, 0, 0, 0);
-}
-
-__device__ __forceinline__ u32x4 lds_read_b128(const char* smem, u32 off) {
-  return *reinterpret_cast<const u32x4*>(smem + off);
-}
-
-__device__ __forceinline__ u32x2 lds_read_tr16(const char* smem, u32 off) {
-  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(smem + off)));
-}
-
-__device__ __forceinline__ u32x2 lds_read_tr8(const char* smem, u32 off) {
-  typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
-  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(smem + off)));
-}
-
-// Workgroup id -> logical tile id such that consecutive logical ids run on the
-// same XCD (hardware hands workgroups to the 8 XCDs round-robin).  Consecutive
-// logical ids are query tiles of one (batch, head), so that slice's K and V
-// are fetched once into that XCD's L2 and reused by its other query tiles.
-__device__ __forceinline__ int xcd_remap(int wg, int total) {
-  constexpr int kXcd = 8;
-  const int xcd = wg % kXcd, pos = wg / kXcd;
-  const int per = total / kXcd, rem = total % kXcd;
-  return xcd < rem ? xcd * (per + 1) + pos : rem * (per + 1) + (xcd - rem) * per + pos;
-}
-
-// LDS tile layouts.  The LDS has 64 four-byte banks (256 bytes per cycle): a
-// 128-bit read is served 16 lanes per cycle and a 64-bit (transposing) read
-// 32 lanes per cycle.  Rows are padded rather than swizzled, so that every
-// operand read of a tile is one per-lane base address plus a compile-time
-// offset (no address arithmetic, and no address registers, per read):
-//   * K rows (read 16 consecutive rows x one 16-byte chunk at a time) are
-//     followed by one 16-byte pad granule, which staggers consecutive rows
-//     by 4 banks (row bytes + 16 is 4 mod 64 words for every row size here).
-//   * V rows are read by the transposing reads as 4 consecutive rows x 64
-//     contiguous bytes (16-bit values) or rows {r..r+3, r+8..r+11} x 32
-//     contiguous bytes (8-bit values); pads after every 1, 2 or 8 rows give
-//     each of those rows its own bank range.  The byte offset of row r is
-//     RB*r + PA*(r >> SA) + PB*(r >> SB); groups of 2^SG rows repeat the same
-//     pattern, and every read's 16-row block offset is a multiple of a group.
-template <int RB, bool FP8>
-struct VLayout {
-  static_assert(RB == 64 || RB == 128 || RB == 256, "row size");
-  static constexpr int PA = FP8 ? 32 : 64;
-  static constexpr int SA = FP8 ? (RB == 64 ? 3 : 1) : (RB == 256 ? 0 : 1);
-  static constexpr int PB = FP8 && RB == 128 ? 64 : 0;
-  static constexpr int SB = 3;
-  static constexpr int SG = PB ? SB : SA;               // log2 rows per group
-  static constexpr int kGroupRows = 1 << SG;
-  __host__ __device__ static constexpr int row(int r) { return RB * r + PA * (r >> SA) + (PB ? PB * (r >> SB) : 0); }
-  static constexpr int kGroupBytes = row(kGroupRows);   // bytes from one group to the next
-  static_assert(kGroupBytes % 16 == 0 && 16 % kGroupRows == 0, "groups of whole granules within 16 rows");
-};
-
-// Software pipeline over a fixed sequence of N matrix instructions whose A
-// operands come from LDS: the operand of instruction i + DEPTH is read right
-// after instruction i issues, so every read has DEPTH instructions' time to
-// land.  Instructions [0, NPV) take two operand reads each, the rest one.
-// The sched_group_barrier sequence pins that order through scheduling (left
-// alone, the scheduler sinks each read next to its use).
-template <int I, int N, int NPV, int DEPTH>
-__device__ __forceinline__ void pipeline_order() {
-  if constexpr (I < N) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one matrix instruction
-    if constexpr (I + DEPTH < N) __builtin_amdgcn_sched_group_barrier(0x100, I + DEPTH < NPV ? 2 : 1, 0);  // its reads
-    pipeline_order<I + 1, N, NPV, DEPTH>();
-  }
-}
-
-template <int N, int NPV, int DEPTH, class Read, class Mma>
-__device__ __forceinline__ void op_pipeline(Read read, Mma mma) {
-  u32x4 buf[DEPTH];
-  constexpr int P = DEPTH < N ? DEPTH : N;
-#pragma unroll
-  for (int i = 0; i < P; ++i) buf[i] = read(i);
-#pragma unroll
-  for (int i = 0; i < N; ++i) {
-    mma(i, buf[i % DEPTH]);
-    if (i + DEPTH < N) buf[i % DEPTH] = read(i + DEPTH);
-  }
-  constexpr int kPro = (P < NPV ? P : NPV) * 2 + (P > NPV ? P - NPV : 0);
-  __builtin_amdgcn_sched_group_barrier(0x100, kPro, 0);  // the first DEPTH operands' reads
-  pipeline_order<0, N, NPV, DEPTH>();
-}
 
 template <class Tr, int D, int QW, int NW, int BC>
 struct Shape {
@@ -292,15 +103,27 @@ __global__ __launch_bounds__(NW * 64, WPE) void fa_fwd_kernel(FwdParams p) {
   const int bh = tile / p.n_qtiles;
   int qt = tile - bh * p.n_qtiles;
   if (CAUSAL) qt = p.n_qtiles - 1 - qt;  // longest rows first
-  const int N = p.N;
+  const int b = bh / p.H, h = bh - b * p.H;
+  // Rows of this (sequence, head) slice.  Packed sequences read their bounds
+  // from cu; an inconsistent pair (negative, decreasing or past the end)
+  // makes the sequence empty, so no access can leave the tensors.
+  int N = p.N, row0 = 0;
+  if (p.cu) {
+    const int s0 = p.cu[b], s1 = p.cu[b + 1];
+    const bool ok = 0 <= s0 && s0 <= s1 && s1 <= p.total && s1 - s0 <= p.N;
+    N = ok ? s1 - s0 : 0;
+    row0 = ok ? s0 : 0;
+  }
   const int q0 = qt * S::kBR;
+  if (q0 >= N) return;  // the whole workgroup: this query tile is past the sequence
   const int qw0 = q0 + wave * QW;  // first query row of this wave
+  const int rowb = p.in_row;       // bytes from one row of the slice to the next
 
-  const u32 slice_k = (u32)N * S::kRK;
-  const u32 slice_v = (u32)N * S::kRV;
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc((const char*)p.q + (size_t)bh * slice_k, slice_k);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc((const char*)p.k + (size_t)bh * slice_k, slice_k);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc((const char*)p.v + (size_t)bh * slice_v, slice_v);
+  const size_t in_base = (size_t)b * p.in_batch + (size_t)h * p.in_head + (size_t)row0 * rowb;
+  const u32 slice_bytes = (u32)N * (u32)rowb;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc((const char*)p.q + in_base, slice_bytes);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc((const char*)p.k + in_base, slice_bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc((const char*)p.v + in_base, slice_bytes);
 
   // ---- Q operands, kept in registers.  Lane (half, l32) of query block qb
   // holds row qw0 + 32*qb + l32; k-group `half` of each instruction step.
@@ -312,7 +135,7 @@ __global__ __launch_bounds__(NW * 64, WPE) void fa_fwd_kernel(FwdParams p) {
     if constexpr (Tr::kFp8) {
 #pragma unroll
       for (int s = 0; s < S::kQSteps; ++s) {
-        const int off = row * S::kRK + 64 * s + 32 * half;
+        const int off = row * rowb + 64 * s + 32 * half;
         const u32x4 x0 = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
         const u32x4 x1 = __builtin_amdgcn_raw_buffer_load_b128(rq, off + 16, 0, 0);
 #pragma unroll
@@ -324,7 +147,7 @@ __global__ __launch_bounds__(NW * 64, WPE) void fa_fwd_kernel(FwdParams p) {
     } else {
 #pragma unroll
       for (int s = 0; s < S::kQSteps; ++s) {
-        u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rq, row * S::kRK + (16 * s + 8 * half) * 2, 0, 0);
+        u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rq, row * rowb + (16 * s + 8 * half) * 2, 0, 0);
 #pragma unroll
         for (int e = 0; e < 4; ++e) x[e] = (x[e] ^ p.q_xor) & p.q_and;
         q16[qb][s] = x;
@@ -347,7 +170,7 @@ __global__ __launch_bounds__(NW * 64, WPE) void fa_fwd_kernel(FwdParams p) {
       const int blk = wave + j * NW;
       const int g = blk * 64 + lane;
       const int r = g / S::kGK, c = g - r * S::kGK;
-      if (blk < S::kBlkK && g < S::kGranK && c < S::kCK) load_lds16(rk, dk + blk * 1024, (k0 + r) * S::kRK + c * 16);
+      if (blk < S::kBlkK && g < S::kGranK && c < S::kCK) load_lds16(rk, dk + blk * 1024, (k0 + r) * rowb + c * 16);
     }
   };
   auto issue_v = [&](int kt, char* dv) __attribute__((always_inline)) {
@@ -365,7 +188,7 @@ __global__ __launch_bounds__(NW * 64, WPE) void fa_fwd_kernel(FwdParams p) {
           r = grp * S::VL::kGroupRows + i;
           c = (off - S::VL::row(i)) / 16;
         }
-      if (blk < S::kBlkV && g < S::kGranV && r >= 0) load_lds16(rv, dv + blk * 1024, (k0 + r) * S::kRV + c * 16);
+      if (blk < S::kBlkV && g < S::kGranV && r >= 0) load_lds16(rv, dv + blk * 1024, (k0 + r) * rowb + c * 16);
     }
   };
 
@@ -742,8 +565,10 @@ __global__ __launch_bounds__(NW * 64, WPE) void fa_fwd_kernel(FwdParams p) {
     const float l_tot = halves_sum(lsum[qb]);
     const float inv = l_tot > 0.f ? p.o_mul / l_tot : 0.f;
     if (qi < N) {
-      if (half == 0) p.lse[(size_t)bh * N + qi] = l_tot > 0.f ? (mref[qb] + __log2f(l_tot)) * kLn2 : -INFINITY;
-      char* orow = (char*)p.o + ((size_t)bh * N + qi) * D * 2;
+      if (half == 0)
+        p.lse[(size_t)b * p.lse_batch + (size_t)h * p.lse_head + row0 + qi] =
+            l_tot > 0.f ? (mref[qb] + __log2f(l_tot)) * kLn2 : -INFINITY;
+      char* orow = (char*)p.o + (size_t)b * p.out_batch + (size_t)h * p.out_head + (size_t)(row0 + qi) * p.out_row;
 #pragma unroll
       for (int db = 0; db < S::kDB; ++db)
 #pragma unroll

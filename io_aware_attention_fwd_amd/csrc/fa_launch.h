@@ -8,19 +8,50 @@
 namespace fa {
 
 // Everything a kernel instance needs, already validated and folded on the host.
+// One slice is the rows of one (sequence, head); byte strides locate it:
+//   dense [B,H,N,d]:      batch = H*N*row, head = N*row, row = d*elem
+//   packed [total,H,d]:   batch = 0, head = d*elem, row = H*d*elem, and the
+//                         sequence's first row cu[b] is added
+// lse is indexed the same way in elements (dense [B,H,N], packed [H,total]).
 struct FwdParams {
   const void* q;
   const void* k;
   const void* v;
   void* o;
   float* lse;
-  int B, H, N;
+  const int* cu;  // packed layout: B+1 sequence offsets (device memory); nullptr for dense
+  int B, H, N;    // N: rows per sequence (dense) or the longest sequence (packed)
+  int total;      // packed layout: rows of the packed tensors
   int n_qtiles;   // ceil(N / rows per workgroup)
   int total_wg;   // n_qtiles * B * H
+  long long in_batch, in_head;    // byte strides of Q, K, V
+  int in_row;
+  long long out_batch, out_head;  // byte strides of O
+  int out_row;
+  long long lse_batch, lse_head;  // element strides of lse
   float c;        // |effective scale| * log2(e); 1 when the effective scale is 0
   uint32_t q_xor; // xor applied to every packed Q word: flips signs when the scale is negative
   uint32_t q_and; // and applied to every packed Q word: 0 when the scale is 0
   float o_mul;    // final multiplier of O (the V descale for fp8, else 1)
+};
+
+// Backward pass over dense [B,H,N,d] tensors (16-bit types).
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const float* lse;
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* delta;  // [B,H,N] workspace: rowsum(dO * O), written by the dQ kernel, read by the dK/dV kernel
+  int B, H, N;
+  int n_blocks;  // ceil(N / rows per workgroup), the same for both kernels
+  int total_wg;  // n_blocks * B * H
+  float c;       // scale * log2(e), signed (may be 0)
+  float scale;   // multiplies dQ and dK at the end
 };
 
 enum class Dtype { F16 = 0, BF16 = 1, FP8 = 2 };
@@ -30,5 +61,11 @@ int rows_per_workgroup(Dtype dt, int d, bool causal, int N);
 
 // Enqueue one forward pass; returns hipSuccess or the launch error.
 hipError_t launch_fwd(Dtype dt, int d, bool causal, const FwdParams& p, hipStream_t stream);
+
+// Rows (queries for dQ, keys for dK/dV) one backward workgroup owns.
+constexpr int kBwdRows = 128;
+
+// Enqueue the backward pass (dQ kernel, then dK/dV kernel, on one stream).
+hipError_t launch_bwd(Dtype dt, int d, bool causal, const BwdParams& p, hipStream_t stream);
 
 }  // namespace fa

@@ -33,7 +33,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 BENCH = os.path.join(ROOT, "bench.py")
 DEFAULT_WORKLOADS = ["8,32,1024,64,f16,0", "8,32,8192,64,f16,0", "8,32,4096,64,bf16,1",
-                     "8,32,8192,64,fp8,0", "8,32,8192,128,bf16,0", "2,16,16384,128,bf16,1"]
+                     "8,32,8192,64,fp8,0", "8,32,8192,128,bf16,0", "2,16,16384,128,bf16,1", "4,32,8192,128,fp8,0"]
 COPY_MIB = 256
 
 
@@ -131,7 +131,7 @@ def main(argv=None):
             results.append(r)
     if args.out:
         with open(args.out, "w") as f:
-            f.write("| workload (B,H,N,d,dtype,causal) | FA_TILE (QW x NW x BC x pingpong x waves/SIMD) | us | TFLOP/s "
+            f.write("| workload (B,H,N,d,dtype,causal) | FA_TILE (QW x NW x BC x schedule x waves/SIMD) | us | TFLOP/s "
                     "| MFMA busy | LDS bank-conflict cycles | LDS active cycles | HBM bytes | HBM GB/s |\n")
             f.write("|---|---|---|---|---|---|---|---|---|\n")
             for r in results:

@@ -40,7 +40,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     declared = _declared_functions()
-    assert declared == ["fa_fwd", "fa_fwd_fp8", "fa_strerror", "fa_version"]
+    assert declared == ["fa_bwd", "fa_fwd", "fa_fwd_fp8", "fa_fwd_varlen", "fa_strerror", "fa_version"]
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.library_path()], capture_output=True, text=True, check=True).stdout
     exported = set(re.findall(r"\bT (fa_\w+)$", out, flags=re.M))
     for name in declared:
@@ -131,6 +131,66 @@ def test_fa_fwd_fp8_rejects(lib, descale, kw, code):
     assert _call8(descale, **kw) == _codes()[code]
 
 
+def _callv(**kw):
+    a = dict(q=BASE, k=BASE + SPAN, v=BASE + 2 * SPAN, o=BASE + 3 * SPAN, lse=BASE + 4 * SPAN, cu=BASE + 5 * SPAN,
+             B=3, H=4, total=1000, max_seqlen=600, d=64, scale=0.125, causal=1, dtype=_lib.FA_DTYPE_BF16, stream=None)
+    a.update(kw)
+    return _lib.fa_fwd_varlen(a["q"], a["k"], a["v"], a["o"], a["lse"], a["cu"], a["B"], a["H"], a["total"],
+                              a["max_seqlen"], a["d"], a["scale"], a["causal"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("case,kw,code", [
+    ("null cu_seqlens", dict(cu=None), "FA_ERR_NULL_PTR"),
+    ("null o", dict(o=None), "FA_ERR_NULL_PTR"),
+    ("B=0", dict(B=0), "FA_ERR_SHAPE"),
+    ("max_seqlen=0", dict(max_seqlen=0), "FA_ERR_SHAPE"),
+    ("total<0", dict(total=-1), "FA_ERR_SHAPE"),
+    # one packed row is H*d*2 bytes; max_seqlen rows of it must stay below 2 GiB
+    ("slice >= 2 GiB", dict(H=64, d=128, max_seqlen=(1 << 31) // (64 * 128 * 2)), "FA_ERR_SHAPE"),
+    ("d=80", dict(d=80), "FA_ERR_HEADDIM"),
+    ("dtype=7", dict(dtype=7), "FA_ERR_DTYPE"),
+    ("scale nan", dict(scale=math.nan), "FA_ERR_SCALE"),
+    ("cu misaligned", dict(cu=BASE + 5 * SPAN + 2), "FA_ERR_ALIGN"),
+    ("v misaligned", dict(v=BASE + 2 * SPAN + 4), "FA_ERR_ALIGN"),
+    ("o is k", dict(o=BASE + SPAN), "FA_ERR_ALIAS"),
+    ("lse inside o", dict(lse=BASE + 3 * SPAN + 256), "FA_ERR_ALIAS"),
+    ("no rows", dict(total=0), "FA_OK"),  # valid: nothing to enqueue, no HIP call
+])
+@no_gpu
+def test_fa_fwd_varlen_rejects(lib, case, kw, code):
+    assert _callv(**kw) == _codes()[code], case
+
+
+def _callb(**kw):
+    a = dict(q=BASE, k=BASE + SPAN, v=BASE + 2 * SPAN, o=BASE + 3 * SPAN, lse=BASE + 4 * SPAN, do=BASE + 5 * SPAN,
+             dq=BASE + 6 * SPAN, dk=BASE + 7 * SPAN, dv=BASE + 8 * SPAN, delta=BASE + 9 * SPAN,
+             B=2, H=4, N=1000, d=64, scale=0.125, causal=1, dtype=_lib.FA_DTYPE_F16, stream=None)
+    a.update(kw)
+    return _lib.fa_bwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"], a["dv"], a["delta"],
+                       a["B"], a["H"], a["N"], a["d"], a["scale"], a["causal"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("case,kw,code", [
+    ("null dout", dict(do=None), "FA_ERR_NULL_PTR"),
+    ("null delta", dict(delta=None), "FA_ERR_NULL_PTR"),
+    ("fp8", dict(dtype=_lib.FA_DTYPE_FP8_E4M3), "FA_ERR_DTYPE"),
+    ("dtype=9", dict(dtype=9), "FA_ERR_DTYPE"),
+    ("N=0", dict(N=0), "FA_ERR_SHAPE"),
+    ("slice >= 2 GiB", dict(N=(1 << 31) // (64 * 2)), "FA_ERR_SHAPE"),
+    ("d=256", dict(d=256), "FA_ERR_HEADDIM"),
+    ("scale inf", dict(scale=math.inf), "FA_ERR_SCALE"),
+    ("dk misaligned", dict(dk=BASE + 7 * SPAN + 8), "FA_ERR_ALIGN"),
+    ("delta misaligned", dict(delta=BASE + 9 * SPAN + 1), "FA_ERR_ALIGN"),
+    ("dq is q", dict(dq=BASE), "FA_ERR_ALIAS"),
+    ("dv inside dout", dict(dv=BASE + 5 * SPAN + 4096), "FA_ERR_ALIAS"),
+    ("delta inside dk", dict(delta=BASE + 7 * SPAN + 64), "FA_ERR_ALIAS"),
+    ("dk overlaps dq", dict(dk=BASE + 6 * SPAN + 2 * 4 * 1000 * 64 * 2 - 16), "FA_ERR_ALIAS"),
+])
+@no_gpu
+def test_fa_bwd_rejects(lib, case, kw, code):
+    assert _callb(**kw) == _codes()[code], case
+
+
 def test_python_wrapper_rejects_mismatched_shapes():
     import torch
     q = torch.zeros(1, 2, 8, 64, dtype=torch.float16)
@@ -138,3 +198,7 @@ def test_python_wrapper_rejects_mismatched_shapes():
         _lib.fwd(q, torch.zeros(1, 2, 9, 64, dtype=torch.float16), q, 0.1)
     with pytest.raises(TypeError):
         _lib.fwd(q.float(), q.float(), q.float(), 0.1)
+    with pytest.raises(TypeError):
+        _lib.fwd_varlen(q[0], q[0], q[0], torch.zeros(3, dtype=torch.int64), 8, 0.1)
+    with pytest.raises(ValueError):
+        _lib.fwd_varlen(q, q, q, torch.zeros(3, dtype=torch.int32), 8, 0.1)
