@@ -61,7 +61,7 @@ enum {
   FA_ERR_DTYPE = -4,    /* dtype is not an fa_dtype value (or is FP8_E4M3 for fa_bwd) */
   FA_ERR_SCALE = -5,    /* scale or a descale is NaN or infinite */
   FA_ERR_ALIGN = -6,    /* q, k, v or o not 16-byte aligned, or lse / cu_seqlens not 4-byte aligned */
-  FA_ERR_ALIAS = -7,    /* o or lse overlaps an input, or o overlaps lse */
+  FA_ERR_ALIAS = -7,    /* an output (o, lse; dq, dk, dv, delta) overlaps an input or another output */
   FA_ERR_HIP = -8       /* the kernel launch reported a HIP error */
 };
 
