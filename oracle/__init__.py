@@ -18,6 +18,7 @@ mutation check); see the module docstrings for the passages followed.
 from .formats import decode, decode_e4m3, decode_bf16_bits, dequantize
 from .attention import attention_slice, attention, attention_varlen, slice_sample
 from .backward import attention_backward_slice, attention_backward
+from .dropout import philox4x32_10, keep_threshold, dropout_bytes, attention_dropout_slice, attention_dropout
 
 __all__ = [
     "decode",
@@ -30,4 +31,9 @@ __all__ = [
     "slice_sample",
     "attention_backward_slice",
     "attention_backward",
+    "philox4x32_10",
+    "keep_threshold",
+    "dropout_bytes",
+    "attention_dropout_slice",
+    "attention_dropout",
 ]

@@ -323,3 +323,125 @@ def pin_bwd_identities(impl_bwd):
 
 
 BACKWARD_PINS = (pin_bwd_identities, pin_bwd_torch_autograd, pin_bwd_finite_differences)
+
+
+# ------------------------------------------------------------------ dropout
+# ``impl`` is a module-like object with the functions of ``oracle/dropout.py``:
+# philox4x32_10, keep_threshold, dropout_bytes, attention_dropout_slice.
+
+def pin_dropout_philox_known_answers(impl):
+    """The generator against the published known-answer vectors."""
+    import json
+    import os
+
+    path = os.path.join(os.path.dirname(__file__), "golden", "philox4x32_10_kat.json")
+    for vec in json.load(open(path))["vectors"]:
+        ctr = np.array([int(x, 16) for x in vec["counter"]], dtype=np.uint64)
+        key = np.array([int(x, 16) for x in vec["key"]], dtype=np.uint64)
+        out = impl.philox4x32_10(ctr, key)
+        assert [int(x) for x in out] == [int(x, 16) for x in vec["output"]], vec
+
+
+def pin_dropout_rate_zero_is_attention(impl):
+    """p = 0 keeps every score with weight 1: the forward oracle's result."""
+    from oracle import attention_slice
+
+    rng = np.random.default_rng(31)
+    q, k, v = _rand(rng, 70, 8), _rand(rng, 70, 8), _rand(rng, 70, 8)
+    for causal in (False, True):
+        o, lse = impl.attention_dropout_slice(q, k, v, 0.4, causal, 0.0, 123, 0, 0)
+        o_ref, lse_ref = attention_slice(q, k, v, 0.4, causal)
+        assert np.allclose(o, o_ref, rtol=0, atol=1e-13)
+        assert np.allclose(lse, lse_ref, rtol=0, atol=1e-13)
+
+
+def pin_dropout_lse_is_undropped(impl):
+    """Dropout acts after the softmax: lse is the forward oracle's for any rate."""
+    from oracle import attention_slice
+
+    rng = np.random.default_rng(32)
+    q, k, v = _rand(rng, 40, 8), _rand(rng, 40, 8), _rand(rng, 40, 8)
+    _, lse = impl.attention_dropout_slice(q, k, v, 0.7, True, 0.5, 9, 3, 5)
+    assert np.allclose(lse, attention_slice(q, k, v, 0.7, True)[1], rtol=0, atol=1e-13)
+
+
+def pin_dropout_structure(impl):
+    """Q = 0 and V = I: P_ij = 1/n_i over the n_i visible keys, so
+    O_ij = [u_ij < t] * (256/t) / n_i exactly, with u the slice's bytes."""
+    n = 48
+    q = np.zeros((n, n))
+    v = np.eye(n)
+    for p, causal, seed, offset, bh in ((0.6, False, 5, 0, 0), (0.1, True, 2**40 + 7, 11, 3),
+                                        (1 - 1 / 256, False, 77, 1, 2)):
+        t = impl.keep_threshold(p)
+        o, _ = impl.attention_dropout_slice(q, q, v, 1.0, causal, p, seed, offset, bh)
+        keep = impl.dropout_bytes(n, n, bh, seed, offset) < t
+        visible = np.arange(n)[None, :] <= np.arange(n)[:, None] if causal else np.ones((n, n), bool)
+        n_i = visible.sum(axis=1, keepdims=True)
+        expect = np.where(keep & visible, (256.0 / t) / n_i, 0.0)
+        assert np.allclose(o, expect, rtol=1e-14, atol=0), (p, causal)
+
+
+def pin_dropout_thresholds(impl):
+    """t = floor(256 (1 - p) + 1/2): fixed values, and invalid rates refused."""
+    for p, t in ((0.0, 256), (0.1, 230), (0.5, 128), (0.25, 192), (1 - 1 / 256, 1), (0.998, 1)):
+        assert impl.keep_threshold(p) == t, (p, t)
+    for bad in (-0.1, 1.0, 0.999, float("nan")):
+        try:
+            impl.keep_threshold(bad)
+        except ValueError:
+            continue
+        raise AssertionError(f"rate {bad} accepted")
+
+
+def pin_dropout_byte_statistics(impl):
+    """Bytes of a large slice are uniform (chi-square over 256 bins) and the
+    kept fraction is t/256 within six standard deviations."""
+    u = impl.dropout_bytes(512, 512, 7, 2024, 0).ravel()
+    counts = np.bincount(u, minlength=256)
+    expect = u.size / 256
+    chi2 = ((counts - expect) ** 2 / expect).sum()
+    assert chi2 < 400, chi2  # 255 degrees of freedom: mean 255, sd 22.6
+    for p in (0.1, 0.5, 0.9):
+        t = impl.keep_threshold(p)
+        frac = (u < t).mean()
+        sd = np.sqrt(t / 256 * (1 - t / 256) / u.size)
+        assert abs(frac - t / 256) < 6 * sd, (p, frac)
+
+
+def pin_dropout_streams_independent(impl):
+    """Changing the row, slice, offset or either half of the seed gives another
+    stream: two streams agree on a byte with probability 1/256."""
+    base = impl.dropout_bytes(64, 256, 3, 0x1234_5678_9ABC, 5)
+    others = [
+        impl.dropout_bytes(64, 256, 4, 0x1234_5678_9ABC, 5),        # slice
+        impl.dropout_bytes(64, 256, 3, 0x1234_5678_9ABC, 6),        # offset
+        impl.dropout_bytes(64, 256, 3, 0x1234_5678_9ABD, 5),        # seed, low word
+        impl.dropout_bytes(64, 256, 3, 0x1235_5678_9ABC, 5),        # seed, high word
+    ]
+    for o in others:
+        agree = (o == base).mean()
+        assert agree < 0.02, agree
+    rows = (base[1:] == base[:-1]).mean()  # neighbouring query rows
+    assert rows < 0.02, rows
+    cols = (base[:, 1:] == base[:, :-1]).mean()  # neighbouring keys
+    assert cols < 0.02, cols
+
+
+def pin_dropout_unbiased(impl):
+    """The mean over many seeds approaches the output without dropout (the
+    scale 256/t makes each kept weight an unbiased estimate)."""
+    from oracle import attention_slice
+
+    rng = np.random.default_rng(33)
+    n, d, p = 8, 4, 0.5
+    q, k, v = _rand(rng, n, d), _rand(rng, n, d), _rand(rng, n, d)
+    runs = np.stack([impl.attention_dropout_slice(q, k, v, 0.5, False, p, s, 0, 0)[0] for s in range(600)])
+    ref = attention_slice(q, k, v, 0.5, False)[0]
+    sem = runs.std(axis=0) / np.sqrt(len(runs))
+    assert np.all(np.abs(runs.mean(axis=0) - ref) < 6 * sem + 1e-12)
+
+
+DROPOUT_PINS = (pin_dropout_philox_known_answers, pin_dropout_thresholds, pin_dropout_rate_zero_is_attention,
+                pin_dropout_lse_is_undropped, pin_dropout_structure, pin_dropout_byte_statistics,
+                pin_dropout_streams_independent, pin_dropout_unbiased)

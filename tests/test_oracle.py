@@ -177,3 +177,53 @@ def test_fully_masked_row_reading():
     # not reachable with equal query/key lengths; a key-less query gives O = 0, lse = -inf
     o, lse = oracle.attention_slice(np.ones((2, 4)), np.ones((0, 4)), np.ones((0, 4)), 1.0, False)
     assert not o.any() and np.isneginf(lse).all()
+
+
+DROP_SRC = os.path.join(os.path.dirname(os.path.dirname(__file__)), "oracle", "dropout.py")
+
+
+@pytest.mark.parametrize("pin", pins.DROPOUT_PINS, ids=lambda f: f.__name__)
+def test_dropout_oracle_passes_pin(pin):
+    from oracle import dropout
+
+    pin(dropout)
+
+
+DROPOUT_MUTANTS = {
+    "multipliers swapped": ("prod0 = np.uint64(PHILOX_M0) * c0", "prod0 = np.uint64(PHILOX_M1) * c0"),
+    "key not bumped": ("k0 = (k0 + np.uint64(PHILOX_W0)) & _LOW32", "k0 = k0"),
+    "high and low halves swapped": ("(prod1 >> _SHIFT32) ^ c1 ^ k0, prod1 & _LOW32",
+                                    "(prod1 & _LOW32) ^ c1 ^ k0, prod1 >> _SHIFT32"),
+    "nine rounds": ("for _ in range(10):", "for _ in range(9):"),
+    "threshold truncated": ("math.floor(256.0 * (1.0 - p) + 0.5)", "math.floor(256.0 * (1.0 - p))"),
+    "kept on equality": ("keep = dropout_bytes(n_q, n_k, bh, seed, offset) < t",
+                         "keep = dropout_bytes(n_q, n_k, bh, seed, offset) <= t"),
+    "no rescale": ("o = ((p * keep) @ v) * (256.0 / t)", "o = ((p * keep) @ v)"),
+    "rescale by 1/(1-p)": ("o = ((p * keep) @ v) * (256.0 / t)", "o = ((p * keep) @ v) / (1.0 - p_drop)"),
+    "dropout before normalising": ("p[seen] /= l[seen][:, None]",
+                                   "p *= dropout_bytes(n_q, n_k, bh, seed, offset) < keep_threshold(p_drop); "
+                                   "l = p.sum(axis=1); p[seen] /= l[seen][:, None]"),
+    "row not in counter": ("ctr[..., 1] = i[:, None]", "ctr[..., 1] = 0"),
+    "slice not in counter": ("ctr[..., 2] = bh", "ctr[..., 2] = 0"),
+    "offset ignored": ("ctr[..., 3] = offset & 0xFFFFFFFF", "ctr[..., 3] = 0"),
+    "seed high word ignored": ("(seed >> 32) & 0xFFFFFFFF", "0"),
+    "one call per 32 keys": ("w = words[:, 2 * g + s, q]", "w = words[:, 2 * g, q]"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(DROPOUT_MUTANTS))
+def test_dropout_pins_catch_planted_mistake(name):
+    old, new = DROPOUT_MUTANTS[name]
+    src = open(DROP_SRC).read()
+    assert src.count(old) >= 1, f"mutation site {old!r} not found"
+    mod = types.ModuleType("oracle_dropout_mutant")
+    exec(compile(src.replace(old, new), "oracle_dropout_mutant", "exec"), mod.__dict__)
+    caught = False
+    for pin in pins.DROPOUT_PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin(mod)
+        except Exception:  # an assertion or a crash both count as caught
+            caught = True
+            break
+    assert caught, f"mutant '{name}' passed every dropout pin"
