@@ -295,6 +295,9 @@ def main(argv=None):
     ap.add_argument("--bwd", default=None,
                     help="B,H,N,d,dtype,causal: time the backward pass fa_bwd (after one forward call that "
                          "produces O and lse) instead of the headline shape")
+    ap.add_argument("--dropout", default=None,
+                    help="B,H,N,d,dtype,causal,p: time fa_fwd_dropout at drop rate p (seed 1234, offset 0) "
+                         "instead of the headline shape")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="also run one device copy of this many MiB (reference kernel for HBM counters)")
     args = ap.parse_args(argv)
@@ -314,6 +317,8 @@ def main(argv=None):
         return main_varlen(args)
     if args.bwd:
         return main_bwd(args)
+    if args.dropout:
+        return main_dropout(args)
 
     B, H, N, d, dtype, causal = 8, 32, 1024, 64, "f16", False
     if args.shape:
@@ -491,6 +496,51 @@ def main_varlen(args):
     if not args.no_cpu:
         progress("cpu baseline (oracle)")
         line["cpu_baseline"] = cpu_baseline_varlen(keep[0], keep[1], causal, scale, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+    del torch
+    return 0
+
+
+def main_dropout(args):
+    """The forward pass with dropout on one dense shape (FLOPs as the forward's)."""
+    import torch
+
+    from io_aware_attention_fwd_amd import _lib
+
+    f = args.dropout.split(",")
+    B, H, N, d, dtype, causal, p = (int(f[0]), int(f[1]), int(f[2]), int(f[3]), f[4], f[5] in ("1", "true"),
+                                    float(f[6]))
+    scale = 1.0 / math.sqrt(d)
+    progress(f"dropout inputs B={B} H={H} N={N} d={d} {dtype} causal={int(causal)} p={p}")
+    _, stream, keep = make_call(B, H, N, d, dtype, causal, scale)
+    _, q, k, v, o, lse = keep
+    dt = {"f16": _lib.FA_DTYPE_F16, "bf16": _lib.FA_DTYPE_BF16}[dtype]
+    lib = _lib.load()
+    a = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, N, d, scale, int(causal), dt,
+         p, 1234, 0, stream.cuda_stream)
+
+    def call():
+        rc = lib.fa_fwd_dropout(*a)
+        if rc:
+            raise _lib.FaError(rc, "fa_fwd_dropout")
+    ms = time_calls(call, args.warmup, args.steps, stream)
+    fl = flops(B, H, N, d, causal)
+    peak = PEAK_TFLOPS[dtype]
+    per_call = summarize(time_each(call, 2, min(args.steps, 50), stream), fl, peak)
+    tflops = fl / (ms * 1e-3) / 1e12
+    line = {
+        "metric": "attention fwd TFLOPS + ms at B=8,H=32,d=64,N=512..8192; % of MFMA peak",
+        "value": round(tflops, 2), "unit": "TFLOPS", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5), "per_call": per_call, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": dtype,
+        "data": f"synthetic: i.i.d. N(0,1) inputs from seed 0, stored as {dtype}; dropout seed 1234, offset 0",
+        "config": {"workload": f"attention forward with dropout p={p} B={B} H={H} N={N} d={d} {dtype} "
+                               f"{'causal' if causal else 'non-causal'} scale=1/sqrt({d})",
+                   "B": B, "H": H, "N": N, "d": d, "causal": causal, "p_drop": p},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(tflops / peak, 4), "traffic": None},
+        "timing": "HIP events on the kernel's stream; value = K back-to-back calls / elapsed",
+    }
     print(json.dumps(line), flush=True)
     del torch
     return 0

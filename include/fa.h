@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define FA_VERSION 200 /* major * 10000 + minor * 100 + patch: 0.2.0 */
+#define FA_VERSION 300 /* major * 10000 + minor * 100 + patch: 0.3.0 */
 
 /* Storage format of q, k, v. */
 typedef enum {
@@ -62,7 +62,8 @@ enum {
   FA_ERR_SCALE = -5,    /* scale or a descale is NaN or infinite */
   FA_ERR_ALIGN = -6,    /* q, k, v or o not 16-byte aligned, or lse / cu_seqlens not 4-byte aligned */
   FA_ERR_ALIAS = -7,    /* an output (o, lse; dq, dk, dv, delta) overlaps an input or another output */
-  FA_ERR_HIP = -8       /* the kernel launch reported a HIP error */
+  FA_ERR_HIP = -8,      /* the kernel launch reported a HIP error */
+  FA_ERR_DROPOUT = -9   /* fa_fwd_dropout: p_drop NaN, outside [0, 1), or keeping no score (t = 0) */
 };
 
 /*
@@ -128,6 +129,33 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
 int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
                   const int* cu_seqlens, int B, int H, int total, int max_seqlen,
                   int d, float scale, int causal, int dtype, void* stream);
+
+/*
+ * fa_fwd_dropout -- fa_fwd with dropout on the probabilities.  The tuning
+ * dict of page "从RTX 3090到H100：FlashAttention在NVIDIA各代GPU架构上的性能全景
+ * 分析", section 3.2, carries a dropout rate and notes that a non-zero rate
+ * needs special handling; the pages define nothing further, so:
+ *   O_i = sum_j (P_ij * M_ij * 256 / t) V_j,   lse as for fa_fwd (no dropout),
+ * with t = floor(256 * (1 - p_drop) + 1/2) and M_ij = 1 iff the generator
+ * byte u_ij of the score is below t (keep probability t / 256 exactly, so the
+ * expected output is fa_fwd's).  u_ij comes from Philox4x32-10 (Salmon,
+ * Moraes, Dror, Shaw, "Parallel random numbers: as easy as 1, 2, 3", SC 2011)
+ * with key (seed mod 2^32, seed div 2^32): writing the key column as
+ * j = 32g + 8q + 4s + u (s in {0, 1}; q, u in 0..3), the counter is
+ * (2g + s, i, b*H + h, offset) and u_ij is bits 8u..8u+7 of output word q.
+ * The same (seed, offset) gives the same mask on every call.
+ *
+ *   q, k, v, o, lse, B, H, N, d, scale, causal, stream  as for fa_fwd.
+ *   dtype   F16 or BF16 (FP8_E4M3 returns FA_ERR_DTYPE).
+ *   p_drop  drop rate in [0, 1) with t >= 1 (p_drop <= 1 - 1/512); 0 gives
+ *           fa_fwd's result bit for bit.  Otherwise FA_ERR_DROPOUT.
+ *   seed    the 64-bit Philox key.
+ *   offset  counter word 3: calls that must draw independent masks with one
+ *           seed use different offsets.
+ */
+int fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int H, int N, int d, float scale, int causal, int dtype,
+                   float p_drop, unsigned long long seed, unsigned int offset, void* stream);
 
 /*
  * fa_bwd -- gradients of fa_fwd: given the output gradient dO, write dQ, dK

@@ -1,9 +1,9 @@
 """ctypes binding of libfa.so: argument marshalling only.
 
-``fa_fwd``, ``fa_fwd_fp8``, ``fa_fwd_varlen``, ``fa_bwd``, ``fa_strerror``
-and ``fa_version`` take the same arguments as the C functions declared in
-``include/fa.h`` (device pointers as Python ints, the stream as a
-``hipStream_t`` int or None).  ``fwd``, ``fwd_varlen`` and ``bwd`` allocate
+``fa_fwd``, ``fa_fwd_fp8``, ``fa_fwd_varlen``, ``fa_fwd_dropout``, ``fa_bwd``,
+``fa_strerror`` and ``fa_version`` take the same arguments as the C functions
+declared in ``include/fa.h`` (device pointers as Python ints, the stream as a
+``hipStream_t`` int or None).  ``fwd``, ``fwd_varlen``, ``fwd_dropout`` and ``bwd`` allocate
 their outputs (and the backward workspace) with torch on the inputs' device
 and call the library on torch's current stream.  Every step of the computation runs
 in the library's HIP kernels; if the library is missing or fails to load, the
@@ -52,6 +52,9 @@ def load() -> ctypes.CDLL:
     lib.fa_fwd_fp8.restype = ci
     lib.fa_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, cf, ci, ci, vp]
     lib.fa_fwd_varlen.restype = ci
+    lib.fa_fwd_dropout.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, cf, ci, ci, cf, ctypes.c_ulonglong,
+                                   ctypes.c_uint, vp]
+    lib.fa_fwd_dropout.restype = ci
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, cf, ci, ci, vp]
     lib.fa_bwd.restype = ci
     lib.fa_strerror.argtypes = [ci]
@@ -73,6 +76,10 @@ def fa_fwd_fp8(q, k, v, o, lse, B, H, N, d, scale, causal, q_descale, k_descale,
 def fa_fwd_varlen(q, k, v, o, lse, cu_seqlens, B, H, total, max_seqlen, d, scale, causal, dtype, stream) -> int:
     return load().fa_fwd_varlen(q, k, v, o, lse, cu_seqlens, B, H, total, max_seqlen, d, scale, int(causal), dtype,
                                 stream)
+
+
+def fa_fwd_dropout(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, p_drop, seed, offset, stream) -> int:
+    return load().fa_fwd_dropout(q, k, v, o, lse, B, H, N, d, scale, int(causal), dtype, p_drop, seed, offset, stream)
 
 
 def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, scale, causal, dtype, stream) -> int:
@@ -126,6 +133,30 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: float, causal:
                     B, H, N, d, float(scale), causal, dt, s)
     if rc != 0:
         raise FaError(rc)
+    return out, lse
+
+
+def fwd_dropout(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: float, causal: bool, p_drop: float,
+                seed: int, offset: int = 0, *, stream: torch.cuda.Stream | None = None):
+    """Attention forward with dropout on [B, H, N, d] binary16/bfloat16 device
+    tensors; returns (O, lse).  The mask is a function of (seed, offset) and
+    the score's position (see ``fa_fwd_dropout`` in include/fa.h)."""
+    if q.dtype not in (torch.float16, torch.bfloat16) or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError(f"unsupported dtypes {q.dtype}, {k.dtype}, {v.dtype}")
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError(f"q, k, v must share one [B, H, N, d] shape, got {tuple(q.shape)}, {tuple(k.shape)}, {tuple(v.shape)}")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k, v must be contiguous")
+    B, H, N, d = q.shape
+    out = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    rc = fa_fwd_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, d,
+                        float(scale), causal, _TORCH_DTYPES[q.dtype], float(p_drop), int(seed), int(offset),
+                        stream.cuda_stream)
+    if rc != 0:
+        raise FaError(rc, "fa_fwd_dropout")
     return out, lse
 
 

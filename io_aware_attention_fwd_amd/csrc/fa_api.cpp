@@ -31,8 +31,16 @@ struct Layout {
   int B, H, N, total, d;
 };
 
+// Dropout settings of one call: t = 256 keeps every score (no dropout).
+struct Dropout {
+  uint32_t t;
+  uint64_t seed;
+  uint32_t offset;
+};
+constexpr Dropout kNoDropout{256u, 0u, 0u};
+
 int forward(const void* q, const void* k, const void* v, void* o, float* lse, const Layout& L, float scale, int causal,
-            fa::Dtype dt, float q_descale, float k_descale, float v_descale, void* stream) {
+            fa::Dtype dt, float q_descale, float k_descale, float v_descale, const Dropout& drop, void* stream) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL_PTR;
   const bool packed = L.cu != nullptr;
   if (L.B < 1 || L.H < 1 || L.N < 1 || (packed && L.total < 0)) return FA_ERR_SHAPE;
@@ -41,7 +49,7 @@ int forward(const void* q, const void* k, const void* v, void* o, float* lse, co
   if (!isfinite(scale) || !isfinite(q_descale) || !isfinite(k_descale) || !isfinite(v_descale)) return FA_ERR_SCALE;
   const int eb = elem_bytes(dt);
   const int ob = 2;  // O is binary16 / bfloat16 (bfloat16 for fp8 inputs)
-  const int br = fa::rows_per_workgroup(dt, d, causal != 0, L.N);
+  const int br = fa::rows_per_workgroup(dt, d, causal != 0, L.N, drop.t < 256);
   // The rows of one (sequence, head), plus the padding rows of its last tile,
   // must be addressable with 32-bit byte offsets (the kernels use buffer loads).
   const int64_t in_row = packed ? (int64_t)L.H * d * eb : (int64_t)d * eb;
@@ -101,7 +109,11 @@ int forward(const void* q, const void* k, const void* v, void* o, float* lse, co
   p.q_and = eff == 0 ? 0u : 0xFFFFFFFFu;
   p.c = eff == 0 ? 1.0f : (float)(fabs(eff) * (double)kLog2e);
   if (!isfinite(p.c)) return FA_ERR_SCALE;
-  p.o_mul = v_descale;
+  p.o_mul = v_descale * (float)(256.0 / drop.t);
+  p.drop_t = drop.t;
+  p.seed_lo = (uint32_t)drop.seed;
+  p.seed_hi = (uint32_t)(drop.seed >> 32);
+  p.drop_offset = drop.offset;
 
   if (packed && L.total == 0) return FA_OK;  // no rows: nothing to compute
   if (fa::launch_fwd(dt, d, causal != 0, p, static_cast<hipStream_t>(stream)) != hipSuccess) return FA_ERR_HIP;
@@ -173,13 +185,13 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
     return FA_ERR_DTYPE;
   }
   return forward(q, k, v, o, lse, Layout{nullptr, B, H, N, 0, d}, scale, causal, static_cast<fa::Dtype>(dtype), 1.0f,
-                 1.0f, 1.0f, stream);
+                 1.0f, 1.0f, kNoDropout, stream);
 }
 
 int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
                float scale, int causal, float q_descale, float k_descale, float v_descale, void* stream) {
   return forward(q, k, v, o, lse, Layout{nullptr, B, H, N, 0, d}, scale, causal, fa::Dtype::FP8, q_descale, k_descale,
-                 v_descale, stream);
+                 v_descale, kNoDropout, stream);
 }
 
 int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse, const int* cu_seqlens, int B,
@@ -190,7 +202,20 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* l
     return FA_ERR_DTYPE;
   }
   return forward(q, k, v, o, lse, Layout{cu_seqlens, B, H, max_seqlen, total, d}, scale, causal,
-                 static_cast<fa::Dtype>(dtype), 1.0f, 1.0f, 1.0f, stream);
+                 static_cast<fa::Dtype>(dtype), 1.0f, 1.0f, 1.0f, kNoDropout, stream);
+}
+
+int fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+                   float scale, int causal, int dtype, float p_drop, unsigned long long seed, unsigned int offset,
+                   void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL_PTR;
+  if (dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
+  // t = floor(256 (1 - p) + 1/2), exact in binary64 for a binary32 p in [0, 1)
+  if (!(p_drop >= 0.0f && p_drop < 1.0f)) return FA_ERR_DROPOUT;
+  const double t = floor(256.0 * (1.0 - (double)p_drop) + 0.5);
+  if (t < 1.0) return FA_ERR_DROPOUT;
+  return forward(q, k, v, o, lse, Layout{nullptr, B, H, N, 0, d}, scale, causal, static_cast<fa::Dtype>(dtype), 1.0f,
+                 1.0f, 1.0f, Dropout{(uint32_t)t, (uint64_t)seed, (uint32_t)offset}, stream);
 }
 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout, void* dq,
@@ -211,6 +236,7 @@ const char* fa_strerror(int code) {
     case FA_ERR_ALIGN: return "misaligned pointer: q, k, v, o need 16 bytes, lse and cu_seqlens 4 bytes";
     case FA_ERR_ALIAS: return "an output overlaps an input or the other output";
     case FA_ERR_HIP: return "the kernel launch reported a HIP error";
+    case FA_ERR_DROPOUT: return "dropout rate outside [0, 1), NaN, or so close to 1 that no score is kept";
     default: return "unknown error code";
   }
 }

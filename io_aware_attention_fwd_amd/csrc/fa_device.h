@@ -81,6 +81,30 @@ __device__ __forceinline__ u32 pack_p(float lo, float hi) {
 __device__ __forceinline__ void swap_halves(u32& a, u32& b) {
   asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
 }
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as
+// easy as 1, 2, 3", SC 2011): ten rounds over a 128-bit counter with a
+// 64-bit key.  A round multiplies counter words 0 and 2 by the two Philox
+// constants, swaps the high halves (xored with the other counter words and
+// the key) into words 0 and 2 and the low halves into 3 and 1; the key grows
+// by the two Weyl constants between rounds.  Each 32 x 32 -> 64-bit product is
+// one v_mad_u64_u32.
+__device__ __forceinline__ u32x4 philox4x32_10(u32 c0, u32 c1, u32 c2, u32 c3, u32 k0, u32 k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+    const u32 n0 = (u32)(p1 >> 32) ^ c1 ^ k0;
+    const u32 n2 = (u32)(p0 >> 32) ^ c3 ^ k1;
+    c1 = (u32)p1;
+    c3 = (u32)p0;
+    c0 = n0;
+    c2 = n2;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return u32x4{c0, c1, c2, c3};
+}
+
 __device__ __forceinline__ float halves_max(float x) {
   u32 a = __builtin_bit_cast(u32, x), b = a;
   swap_halves(a, b);

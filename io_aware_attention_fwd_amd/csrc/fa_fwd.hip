@@ -79,7 +79,9 @@ struct Shape {
 // host-side launch stub is emitted.
 // SCHED: 0 = plain (every wave runs Q K^T, softmax, P V of a tile in turn),
 //        1 = ping-pong between wave groups.
-template <class Tr, int D, bool CAUSAL, int QW, int NW, int BC, int SCHED, int WPE>
+// DROP: dropout on the probabilities (kept iff the score's Philox byte is
+// below p.drop_t; the 256/t rescale is part of p.o_mul).
+template <class Tr, int D, bool CAUSAL, int QW, int NW, int BC, int SCHED, int WPE, bool DROP>
 __global__ __launch_bounds__(NW * 64, WPE) void fa_fwd_kernel(FwdParams p) {
   constexpr bool PP = SCHED == 1;
   static_assert(!PP || NW == 8, "the ping-pong schedule pairs waves w and w+4 on one SIMD");
@@ -315,14 +317,24 @@ __global__ __launch_bounds__(NW * 64, WPE) void fa_fwd_kernel(FwdParams p) {
     }
   };
 
-  // ---- probabilities P = exp2(S*c - m) as 16-bit pairs, row sums
-  auto exp_tile = [&](SArr& sc) __attribute__((always_inline)) {
+  // ---- probabilities P = exp2(S*c - m) as 16-bit pairs, row sums.  With
+  // dropout, one Philox call per lane and 32-key block gives the 16 bytes of
+  // the lane's 16 scores: element r of the accumulator (key 8*(r/4) +
+  // 4*half + r%4 of the block) takes byte r, i.e. bits 8*(r%4).. of word r/4.
+  // The counter is (2 * block + half, query row, slice, offset).  Dropped
+  // probabilities are zeroed in the P operand only: the row sum (and so the
+  // normaliser and lse) is that of the whole row.
+  auto exp_tile = [&](int kt, SArr& sc) __attribute__((always_inline)) {
 #pragma unroll
     for (int qb = 0; qb < S::kQB; ++qb) {
       const float mb = mref[qb] == -INFINITY ? 0.f : mref[qb];
       float rs[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kb = 0; kb < S::kKB; ++kb)
+      for (int kb = 0; kb < S::kKB; ++kb) {
+        u32x4 rnd{};
+        if constexpr (DROP)
+          rnd = philox4x32_10(2u * (u32)(kt * S::kKB + kb) + (u32)half, (u32)(qw0 + 32 * qb + l32), (u32)bh,
+                              p.drop_offset, p.seed_lo, p.seed_hi);
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -330,9 +342,18 @@ __global__ __launch_bounds__(NW * 64, WPE) void fa_fwd_kernel(FwdParams p) {
             const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][qb][8 * t + 2 * e], c, -mb));
             const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][qb][8 * t + 2 * e + 1], c, -mb));
             const u32 w = pack_p<kBf>(p0, p1);
-            pb[kb][qb][t][e] = w;
+            if constexpr (DROP) {
+              // elements 8t+2e and 8t+2e+1: word 2t + e/2, bytes 2*(e%2) and 2*(e%2)+1
+              const u32 word = rnd[2 * t + (e >> 1)] >> (16 * (e & 1));
+              const u32 keep = ((word & 0xFFu) < p.drop_t ? 0x0000FFFFu : 0u) |
+                               (((word >> 8) & 0xFFu) < p.drop_t ? 0xFFFF0000u : 0u);
+              pb[kb][qb][t][e] = w & keep;
+            } else {
+              pb[kb][qb][t][e] = w;
+            }
             rs[e] = sum_pair<kBf>(w, p0, p1, rs[e]);
           }
+      }
       lsum[qb] += (rs[0] + rs[1]) + (rs[2] + rs[3]);
     }
   };
@@ -340,7 +361,7 @@ __global__ __launch_bounds__(NW * 64, WPE) void fa_fwd_kernel(FwdParams p) {
   auto softmax = [&](int kt) __attribute__((always_inline)) {
     mask_tile(kt, sacc);
     max_rescale(sacc);
-    exp_tile(sacc);
+    exp_tile(kt, sacc);
   };
 
   // ---- V^T operands.  Element e of lane (half, col) of the V^T operand is
@@ -590,16 +611,17 @@ struct Variant {
   int qw, nw, bc, sched, wpe;  // rows per wave, waves, keys per tile, schedule, min waves per SIMD
 };
 
-template <class Tr, int D, bool CAUSAL, int QW, int NW, int BC, int SCHED, int WPE>
+template <class Tr, int D, bool CAUSAL, int QW, int NW, int BC, int SCHED, int WPE, bool DROP>
 hipError_t launch_one(const FwdParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL((fa_fwd_kernel<Tr, D, CAUSAL, QW, NW, BC, SCHED, WPE>), dim3(p.total_wg), dim3(NW * 64), 0,
+  hipLaunchKernelGGL((fa_fwd_kernel<Tr, D, CAUSAL, QW, NW, BC, SCHED, WPE, DROP>), dim3(p.total_wg), dim3(NW * 64), 0,
                      stream, p);
   return hipGetLastError();
 }
 
 // Tile shapes compiled for every (dtype, d, causal).  FA_TILE=<qw>x<nw>x<bc>x<sched>x<wpe>
 // selects one of them instead of the default (tile sweeps only; an unknown
-// value falls back to the default).
+// value falls back to the default).  Dropout kernels exist for the default
+// shapes only, so FA_TILE is ignored with dropout.
 constexpr Variant kVariants[] = {{32, 8, 64, 1, 2}, {32, 4, 64, 0, 4}, {32, 4, 64, 0, 3}, {32, 4, 64, 0, 2},
                                  {64, 4, 64, 0, 2}};
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
@@ -615,8 +637,8 @@ int default_variant(Dtype dt, int d, bool causal, int N) {
   return 2;                               // plain, three waves per SIMD
 }
 
-int selected_variant(Dtype dt, int d, bool causal, int N) {
-  const char* env = getenv("FA_TILE");
+int selected_variant(Dtype dt, int d, bool causal, int N, bool dropout) {
+  const char* env = dropout ? nullptr : getenv("FA_TILE");
   if (env) {
     Variant v{};
     if (sscanf(env, "%dx%dx%dx%dx%d", &v.qw, &v.nw, &v.bc, &v.sched, &v.wpe) == 5)
@@ -631,25 +653,50 @@ int selected_variant(Dtype dt, int d, bool causal, int N) {
 template <class Tr, int D, bool CAUSAL>
 hipError_t dispatch_variant(int v, const FwdParams& p, hipStream_t stream) {
   switch (v) {
-    case 1: return launch_one<Tr, D, CAUSAL, 32, 4, 64, 0, 4>(p, stream);
-    case 2: return launch_one<Tr, D, CAUSAL, 32, 4, 64, 0, 3>(p, stream);
-    case 3: return launch_one<Tr, D, CAUSAL, 32, 4, 64, 0, 2>(p, stream);
-    case 4: return launch_one<Tr, D, CAUSAL, 64, 4, 64, 0, 2>(p, stream);
-    default: return launch_one<Tr, D, CAUSAL, 32, 8, 64, 1, 2>(p, stream);
+    case 1: return launch_one<Tr, D, CAUSAL, 32, 4, 64, 0, 4, false>(p, stream);
+    case 2: return launch_one<Tr, D, CAUSAL, 32, 4, 64, 0, 3, false>(p, stream);
+    case 3: return launch_one<Tr, D, CAUSAL, 32, 4, 64, 0, 2, false>(p, stream);
+    case 4: return launch_one<Tr, D, CAUSAL, 64, 4, 64, 0, 2, false>(p, stream);
+    default: return launch_one<Tr, D, CAUSAL, 32, 8, 64, 1, 2, false>(p, stream);
   }
+}
+
+// Dropout: only the shapes default_variant picks for the 16-bit types
+// (d = 128: ping-pong; d = 64: 32 rows per wave, or 64 without the causal mask).
+template <class Tr, int D, bool CAUSAL>
+hipError_t dispatch_dropout(int v, const FwdParams& p, hipStream_t stream) {
+  if constexpr (D == 128) {
+    if (v == 0) return launch_one<Tr, D, CAUSAL, 32, 8, 64, 1, 2, true>(p, stream);
+  } else {
+    if (v == 2) return launch_one<Tr, D, CAUSAL, 32, 4, 64, 0, 3, true>(p, stream);
+    if constexpr (!CAUSAL) {
+      if (v == 4) return launch_one<Tr, D, CAUSAL, 64, 4, 64, 0, 2, true>(p, stream);
+    }
+  }
+  return hipErrorInvalidValue;
 }
 
 template <class Tr>
 hipError_t dispatch_dtype(Dtype dt, int d, bool causal, const FwdParams& p, hipStream_t stream) {
-  const int v = selected_variant(dt, d, causal, p.N);
+  const bool drop = p.drop_t < 256;
+  const int v = selected_variant(dt, d, causal, p.N, drop);
+  if constexpr (!Tr::kFp8) {
+    if (drop) {
+      if (d == 64)
+        return causal ? dispatch_dropout<Tr, 64, true>(v, p, stream) : dispatch_dropout<Tr, 64, false>(v, p, stream);
+      return causal ? dispatch_dropout<Tr, 128, true>(v, p, stream) : dispatch_dropout<Tr, 128, false>(v, p, stream);
+    }
+  } else {
+    if (drop) return hipErrorInvalidValue;
+  }
   if (d == 64) return causal ? dispatch_variant<Tr, 64, true>(v, p, stream) : dispatch_variant<Tr, 64, false>(v, p, stream);
   return causal ? dispatch_variant<Tr, 128, true>(v, p, stream) : dispatch_variant<Tr, 128, false>(v, p, stream);
 }
 
 }  // namespace
 
-int rows_per_workgroup(Dtype dt, int d, bool causal, int N) {
-  const Variant& v = kVariants[selected_variant(dt, d, causal, N)];
+int rows_per_workgroup(Dtype dt, int d, bool causal, int N, bool dropout) {
+  const Variant& v = kVariants[selected_variant(dt, d, causal, N, dropout)];
   return v.qw * v.nw;
 }
 

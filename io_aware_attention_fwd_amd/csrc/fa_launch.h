@@ -32,7 +32,12 @@ struct FwdParams {
   float c;        // |effective scale| * log2(e); 1 when the effective scale is 0
   uint32_t q_xor; // xor applied to every packed Q word: flips signs when the scale is negative
   uint32_t q_and; // and applied to every packed Q word: 0 when the scale is 0
-  float o_mul;    // final multiplier of O (the V descale for fp8, else 1)
+  float o_mul;    // final multiplier of O (the V descale for fp8, times 256/t with dropout)
+  // Dropout: a score is kept iff its generator byte is below drop_t (1..256;
+  // 256 keeps every score and selects the kernels without dropout).  Philox
+  // key (seed_lo, seed_hi); counter word 3 is drop_offset.
+  uint32_t drop_t;
+  uint32_t seed_lo, seed_hi, drop_offset;
 };
 
 // Backward pass over dense [B,H,N,d] tensors (16-bit types).
@@ -57,7 +62,7 @@ struct BwdParams {
 enum class Dtype { F16 = 0, BF16 = 1, FP8 = 2 };
 
 // Rows of Q one workgroup owns for the instance chosen for this call (sizes the grid).
-int rows_per_workgroup(Dtype dt, int d, bool causal, int N);
+int rows_per_workgroup(Dtype dt, int d, bool causal, int N, bool dropout);
 
 // Enqueue one forward pass; returns hipSuccess or the launch error.
 hipError_t launch_fwd(Dtype dt, int d, bool causal, const FwdParams& p, hipStream_t stream);

@@ -40,7 +40,8 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     declared = _declared_functions()
-    assert declared == ["fa_bwd", "fa_fwd", "fa_fwd_fp8", "fa_fwd_varlen", "fa_strerror", "fa_version"]
+    assert declared == ["fa_bwd", "fa_fwd", "fa_fwd_dropout", "fa_fwd_fp8", "fa_fwd_varlen", "fa_strerror",
+                        "fa_version"]
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.library_path()], capture_output=True, text=True, check=True).stdout
     exported = set(re.findall(r"\bT (fa_\w+)$", out, flags=re.M))
     for name in declared:
@@ -55,7 +56,7 @@ def test_version_matches_header(lib):
 
 def test_strerror_covers_every_code(lib):
     codes = _codes()
-    assert codes["FA_OK"] == 0 and len(codes) == 9
+    assert codes["FA_OK"] == 0 and len(codes) == 10
     texts = {_lib.fa_strerror(c) for c in codes.values()}
     assert len(texts) == len(codes) and "unknown error code" not in texts
     assert _lib.fa_strerror(12345) == "unknown error code"
@@ -129,6 +130,31 @@ def test_fa_fwd_rejects(lib, case, kw, code):
 @no_gpu
 def test_fa_fwd_fp8_rejects(lib, descale, kw, code):
     assert _call8(descale, **kw) == _codes()[code]
+
+
+def _calld(p_drop=0.1, seed=1, offset=0, **kw):
+    a = _args(**kw)
+    return _lib.fa_fwd_dropout(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"], a["d"], a["scale"],
+                               a["causal"], a["dtype"], p_drop, seed, offset, a["stream"])
+
+
+@pytest.mark.parametrize("p_drop,kw,code", [
+    (-0.01, {}, "FA_ERR_DROPOUT"),
+    (1.0, {}, "FA_ERR_DROPOUT"),
+    (math.nan, {}, "FA_ERR_DROPOUT"),
+    (0.999, {}, "FA_ERR_DROPOUT"),  # t = floor(0.256 + 1/2) = 0 keeps nothing
+    (0.1, dict(dtype=_lib.FA_DTYPE_FP8_E4M3), "FA_ERR_DTYPE"),
+    (0.1, dict(dtype=7), "FA_ERR_DTYPE"),
+    (0.1, dict(v=None), "FA_ERR_NULL_PTR"),
+    (0.1, dict(d=96), "FA_ERR_HEADDIM"),
+    (0.1, dict(N=0), "FA_ERR_SHAPE"),
+    (0.1, dict(scale=math.inf), "FA_ERR_SCALE"),
+    (0.1, dict(o=BASE + 3 * SPAN + 4), "FA_ERR_ALIGN"),
+    (0.1, dict(o=BASE + SPAN), "FA_ERR_ALIAS"),
+])
+@no_gpu
+def test_fa_fwd_dropout_rejects(lib, p_drop, kw, code):
+    assert _calld(p_drop, **kw) == _codes()[code]
 
 
 def _callv(**kw):
