@@ -161,6 +161,37 @@ def structured(B: int, H: int, N: int, d: int, dtype: str, period: int = 64) -> 
     return store(dtype, q32, k32, v32)
 
 
+@dataclass
+class ProjectionInputs:
+    """Stored inputs of one QKV projection: x [B, N, D], w [3 H d, D] and
+    bias [3 H d] in the storage format of ``dtype`` (f16 or bf16 bits as in
+    ``Inputs``)."""
+
+    dtype: str
+    x: np.ndarray
+    w: np.ndarray
+    bias: np.ndarray
+    H: int
+    d: int
+
+
+def make_projection(B: int, N: int, D: int, H: int, d: int, dtype: str, seed: int = 0) -> ProjectionInputs:
+    """x ~ N(0, 1), weight ~ N(0, 1/D) (a linear layer's usual initial scale,
+    so that projected values are of order 1) and bias ~ N(0, 0.01), drawn in
+    that order from ``default_rng(seed)`` in float32 and stored as ``dtype``."""
+    if dtype not in ("f16", "bf16"):
+        raise ValueError("the projection takes f16 or bf16")
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal(size=(B, N, D), dtype=np.float32)
+    w = rng.standard_normal(size=(3 * H * d, D), dtype=np.float32) * np.float32(1.0 / np.sqrt(D))
+    bias = rng.standard_normal(size=(3 * H * d,), dtype=np.float32) * np.float32(0.1)
+    if dtype == "f16":
+        cast = lambda a: a.astype(np.float16)
+    else:
+        cast = f32_to_bf16_bits
+    return ProjectionInputs(dtype, cast(x), cast(w), cast(bias), H, d)
+
+
 def nbytes_kv(B: int, H: int, N: int, d: int, elem_bytes: int = 2) -> int:
     """Bytes of one K plus one V tensor of shape [B, H, N, d]."""
     return 2 * B * H * N * d * elem_bytes

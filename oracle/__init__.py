@@ -19,6 +19,7 @@ from .formats import decode, decode_e4m3, decode_bf16_bits, dequantize
 from .attention import attention_slice, attention, attention_varlen, slice_sample
 from .backward import attention_backward_slice, attention_backward
 from .dropout import philox4x32_10, keep_threshold, dropout_bytes, attention_dropout_slice, attention_dropout
+from .projection import qkv_projection
 
 __all__ = [
     "decode",
@@ -36,4 +37,5 @@ __all__ = [
     "dropout_bytes",
     "attention_dropout_slice",
     "attention_dropout",
+    "qkv_projection",
 ]

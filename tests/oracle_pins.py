@@ -445,3 +445,75 @@ def pin_dropout_unbiased(impl):
 DROPOUT_PINS = (pin_dropout_philox_known_answers, pin_dropout_thresholds, pin_dropout_rate_zero_is_attention,
                 pin_dropout_lse_is_undropped, pin_dropout_structure, pin_dropout_byte_statistics,
                 pin_dropout_streams_independent, pin_dropout_unbiased)
+
+
+# ------------------------------------------------------------------ QKV projection
+# ``impl(x, w, bias, H, d) -> (Q, K, V)`` as ``oracle.qkv_projection``.
+
+def pin_proj_brute_force(impl):
+    """Scalar loops over every output element of a tiny case."""
+    rng = np.random.default_rng(41)
+    B, N, D, H, d = 2, 3, 5, 2, 3
+    x = rng.standard_normal((B, N, D))
+    w = rng.standard_normal((3 * H * d, D))
+    bias = rng.standard_normal(3 * H * d)
+    outs = impl(x, w, bias, H, d)
+    for s in range(3):
+        assert outs[s].shape == (B, H, N, d)
+        for b in range(B):
+            for h in range(H):
+                for n in range(N):
+                    for c in range(d):
+                        f = s * H * d + h * d + c
+                        ref = bias[f] + sum(x[b, n, kk] * w[f, kk] for kk in range(D))
+                        assert abs(outs[s][b, h, n, c] - ref) < 1e-12, (s, b, h, n, c)
+
+
+def pin_proj_torch_linear(impl):
+    """torch's float64 linear layer, then view/permute into [3, B, H, N, d]."""
+    rng = np.random.default_rng(42)
+    B, N, D, H, d = 2, 7, 16, 3, 4
+    x = rng.standard_normal((B, N, D))
+    w = rng.standard_normal((3 * H * d, D))
+    bias = rng.standard_normal(3 * H * d)
+    y = torch.nn.functional.linear(torch.tensor(x), torch.tensor(w), torch.tensor(bias))
+    ref = y.view(B, N, 3, H, d).permute(2, 0, 3, 1, 4).numpy()
+    outs = impl(x, w, bias, H, d)
+    for s in range(3):
+        assert np.allclose(outs[s], ref[s], rtol=0, atol=1e-12), s
+    outs = impl(x, w, None, H, d)
+    y = torch.nn.functional.linear(torch.tensor(x), torch.tensor(w))
+    ref = y.view(B, N, 3, H, d).permute(2, 0, 3, 1, 4).numpy()
+    for s in range(3):
+        assert np.allclose(outs[s], ref[s], rtol=0, atol=1e-12), s
+
+
+def pin_proj_one_hot(impl):
+    """One token with one input feature and one weight row: a single 1 lands
+    at the (tensor, batch, head, token, column) the layout names."""
+    B, N, D, H, d = 2, 5, 8, 3, 4
+    for b0, n0, k0, s0, h0, c0 in ((1, 3, 6, 2, 1, 3), (0, 0, 0, 0, 0, 0), (1, 4, 2, 1, 2, 1)):
+        x = np.zeros((B, N, D))
+        x[b0, n0, k0] = 1.0
+        w = np.zeros((3 * H * d, D))
+        w[s0 * H * d + h0 * d + c0, k0] = 1.0
+        outs = impl(x, w, None, H, d)
+        for s in range(3):
+            want = np.zeros((B, H, N, d))
+            if s == s0:
+                want[b0, h0, n0, c0] = 1.0
+            assert np.array_equal(outs[s], want), (s, b0, n0, k0, s0, h0, c0)
+
+
+def pin_proj_bias_only(impl):
+    """x = 0: every token of every batch carries the bias of its feature."""
+    B, N, D, H, d = 2, 3, 4, 2, 5
+    bias = np.arange(3 * H * d, dtype=np.float64)
+    outs = impl(np.zeros((B, N, D)), np.ones((3 * H * d, D)), bias, H, d)
+    for s in range(3):
+        for h in range(H):
+            for c in range(d):
+                assert np.all(outs[s][:, h, :, c] == bias[s * H * d + h * d + c])
+
+
+PROJECTION_PINS = (pin_proj_brute_force, pin_proj_torch_linear, pin_proj_one_hot, pin_proj_bias_only)

@@ -227,3 +227,41 @@ def test_dropout_pins_catch_planted_mistake(name):
             caught = True
             break
     assert caught, f"mutant '{name}' passed every dropout pin"
+
+
+PROJ_SRC = os.path.join(os.path.dirname(os.path.dirname(__file__)), "oracle", "projection.py")
+
+
+@pytest.mark.parametrize("pin", pins.PROJECTION_PINS, ids=lambda f: f.__name__)
+def test_projection_oracle_passes_pin(pin):
+    pin(oracle.qkv_projection)
+
+
+PROJECTION_MUTANTS = {
+    "bias ignored": ("y = y + np.asarray(bias, dtype=np.float64)[None, None, :]", "y = y"),
+    "weight not transposed": ("y = x @ w.T", "y = x @ w.reshape(w.shape[1], w.shape[0])"),
+    "heads and columns swapped": ("y.reshape(B, N, 3, H, d).transpose(2, 0, 3, 1, 4)",
+                                  "y.reshape(B, N, 3, d, H).transpose(2, 0, 4, 1, 3)"),
+    "tokens and heads swapped": ("transpose(2, 0, 3, 1, 4)", "transpose(2, 0, 1, 3, 4).reshape(3, B, H, N, d)"),
+    "per-head interleaved split": ("y.reshape(B, N, 3, H, d).transpose(2, 0, 3, 1, 4)",
+                                   "y.reshape(B, N, H, 3, d).transpose(3, 0, 2, 1, 4)"),
+    "Q and K exchanged": ("return y[0], y[1], y[2]", "return y[1], y[0], y[2]"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(PROJECTION_MUTANTS))
+def test_projection_pins_catch_planted_mistake(name):
+    old, new = PROJECTION_MUTANTS[name]
+    src = open(PROJ_SRC).read()
+    assert src.count(old) >= 1, f"mutation site {old!r} not found"
+    mod = types.ModuleType("oracle_projection_mutant")
+    exec(compile(src.replace(old, new), "oracle_projection_mutant", "exec"), mod.__dict__)
+    caught = False
+    for pin in pins.PROJECTION_PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin(mod.qkv_projection)
+        except Exception:  # an assertion or a crash both count as caught
+            caught = True
+            break
+    assert caught, f"mutant '{name}' passed every projection pin"
