@@ -298,6 +298,9 @@ def main(argv=None):
     ap.add_argument("--dropout", default=None,
                     help="B,H,N,d,dtype,causal,p: time fa_fwd_dropout at drop rate p (seed 1234, offset 0) "
                          "instead of the headline shape")
+    ap.add_argument("--proj", default=None,
+                    help="B,N,D,H,d,dtype: time the fused QKV projection fa_qkv_proj (with bias) instead of the "
+                         "headline shape")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="also run one device copy of this many MiB (reference kernel for HBM counters)")
     args = ap.parse_args(argv)
@@ -319,6 +322,8 @@ def main(argv=None):
         return main_bwd(args)
     if args.dropout:
         return main_dropout(args)
+    if args.proj:
+        return main_proj(args)
 
     B, H, N, d, dtype, causal = 8, 32, 1024, 64, "f16", False
     if args.shape:
@@ -539,6 +544,58 @@ def main_dropout(args):
                    "B": B, "H": H, "N": N, "d": d, "causal": causal, "p_drop": p},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(tflops / peak, 4), "traffic": None},
+        "timing": "HIP events on the kernel's stream; value = K back-to-back calls / elapsed",
+    }
+    print(json.dumps(line), flush=True)
+    del torch
+    return 0
+
+
+def main_proj(args):
+    """The fused QKV projection: FLOPs 2*M*(3Hd)*D, M = B*N tokens."""
+    import torch
+
+    from io_aware_attention_fwd_amd import _lib, gen
+
+    f = args.proj.split(",")
+    B, N, D, H, d, dtype = int(f[0]), int(f[1]), int(f[2]), int(f[3]), int(f[4]), f[5]
+    progress(f"projection inputs B={B} N={N} D={D} H={H} d={d} {dtype}")
+    pi = gen.make_projection(B, N, D, H, d, dtype, seed=0)
+
+    def dev(a):
+        if dtype == "f16":
+            return torch.from_numpy(a).cuda()
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    x, w, bias = dev(pi.x), dev(pi.w), dev(pi.bias)
+    q, k, v = (torch.empty((B, H, N, d), dtype=x.dtype, device="cuda") for _ in range(3))
+    stream = torch.cuda.current_stream()
+    lib = _lib.load()
+    dt = {"f16": _lib.FA_DTYPE_F16, "bf16": _lib.FA_DTYPE_BF16}[dtype]
+    a = (x.data_ptr(), w.data_ptr(), bias.data_ptr(), q.data_ptr(), k.data_ptr(), v.data_ptr(), B, N, D, H, d, dt,
+         stream.cuda_stream)
+
+    def call():
+        rc = lib.fa_qkv_proj(*a)
+        if rc:
+            raise _lib.FaError(rc, "fa_qkv_proj")
+    ms = time_calls(call, args.warmup, args.steps, stream)
+    M, ncol = B * N, 3 * H * d
+    fl = 2.0 * M * ncol * D
+    peak = PEAK_TFLOPS[dtype]
+    per_call = summarize(time_each(call, 2, min(args.steps, 50), stream), fl, peak)
+    tflops = fl / (ms * 1e-3) / 1e12
+    algo_bytes = 2 * (M * D + ncol * D + ncol + M * ncol)
+    line = {
+        "metric": "attention fwd TFLOPS + ms at B=8,H=32,d=64,N=512..8192; % of MFMA peak",
+        "value": round(tflops, 2), "unit": "TFLOPS", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5), "per_call": per_call, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": dtype,
+        "data": f"synthetic: x ~ N(0,1), weight ~ N(0,1/D), bias ~ N(0,0.01) from seed 0, stored as {dtype}",
+        "config": {"workload": f"fused QKV projection B={B} N={N} D={D} -> Q, K, V [B, H={H}, N, d={d}] {dtype}",
+                   "B": B, "N": N, "D": D, "H": H, "d": d},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(tflops / peak, 4), "traffic": None, "algorithmic_bytes_per_launch": algo_bytes,
+                     "algorithmic_hbm_gbs": round(algo_bytes / (ms * 1e-3) / 1e9, 1)},
         "timing": "HIP events on the kernel's stream; value = K back-to-back calls / elapsed",
     }
     print(json.dumps(line), flush=True)

@@ -56,12 +56,13 @@ typedef enum {
 enum {
   FA_OK = 0,
   FA_ERR_NULL_PTR = -1, /* a required pointer (q, k, v, o, lse, cu_seqlens, dout, dq, dk, dv, delta) is NULL */
-  FA_ERR_SHAPE = -2,    /* B, H or N (max_seqlen) < 1, total < 0, a slice of 2 GiB or more, or too many tiles */
+  FA_ERR_SHAPE = -2,    /* B, H or N (max_seqlen) < 1, total < 0, a slice of 2 GiB or more, too many tiles,
+                           or (fa_qkv_proj) D not a positive multiple of 64 */
   FA_ERR_HEADDIM = -3,  /* d is not 64 or 128 */
   FA_ERR_DTYPE = -4,    /* dtype is not an fa_dtype value (or is FP8_E4M3 for fa_bwd) */
   FA_ERR_SCALE = -5,    /* scale or a descale is NaN or infinite */
-  FA_ERR_ALIGN = -6,    /* q, k, v or o not 16-byte aligned, or lse / cu_seqlens not 4-byte aligned */
-  FA_ERR_ALIAS = -7,    /* an output (o, lse; dq, dk, dv, delta) overlaps an input or another output */
+  FA_ERR_ALIGN = -6,    /* a tensor not 16-byte aligned, lse / cu_seqlens / delta not 4-byte, bias not 8-byte */
+  FA_ERR_ALIAS = -7,    /* an output (o, lse; dq, dk, dv, delta; q, k, v of fa_qkv_proj) overlaps an input or another output */
   FA_ERR_HIP = -8,      /* the kernel launch reported a HIP error */
   FA_ERR_DROPOUT = -9   /* fa_fwd_dropout: p_drop NaN, outside [0, 1), or keeping no score (t = 0) */
 };
@@ -179,6 +180,26 @@ int fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
            const void* dout, void* dq, void* dk, void* dv, float* delta,
            int B, int H, int N, int d, float scale, int causal, int dtype, void* stream);
+
+/*
+ * fa_qkv_proj -- the fused input projection ahead of attention: page
+ * "FlashAttention与TensorRT 10集成", section "算子融合的极致优化", item 1,
+ * merges the projection with the transpose and rearrangement into one
+ * kernel.  For the layer input X and one packed weight W of the three
+ * projections (stored [out, in], as a linear layer's):
+ *   Y = X W^T + bias,   out_s[b, h, n, c] = Y[b, n, s*H*d + h*d + c]
+ * with s = 0, 1, 2 writing q, k, v.  The outputs are exactly fa_fwd's inputs.
+ *
+ *   x        [B, N, D] token-major, F16 or BF16.
+ *   w        [3*H*d, D], same dtype.
+ *   bias     [3*H*d], same dtype, or NULL for none.
+ *   q, k, v  outputs, each [B, H, N, d], same dtype (rounded from float32).
+ *   B, N, H  >= 1; D a multiple of 64 (>= 64); d = 64 or 128.
+ * x, w, q, k, v need 16-byte alignment, bias 8; outputs may not overlap the
+ * inputs or each other.  X and W must each stay below 2 GiB.
+ */
+int fa_qkv_proj(const void* x, const void* w, const void* bias, void* q, void* k, void* v,
+                int B, int N, int D, int H, int d, int dtype, void* stream);
 
 /* Static description of a return code; never NULL. */
 const char* fa_strerror(int code);

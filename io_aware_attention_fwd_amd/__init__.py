@@ -1,9 +1,9 @@
 """MI355X (gfx950) FlashAttention forward: Python side of the C-ABI library.
 
 ``fa_fwd`` / ``fa_fwd_fp8`` / ``fa_fwd_varlen`` / ``fa_fwd_dropout`` /
-``fa_bwd`` mirror the C entry points in ``include/fa.h`` and only marshal
-arguments; ``fwd``, ``fwd_varlen``, ``fwd_dropout`` and ``bwd`` are
-convenience wrappers that allocate the outputs with torch and call them.  The
+``fa_bwd`` / ``fa_qkv_proj`` mirror the C entry points in ``include/fa.h`` and
+only marshal arguments; ``fwd``, ``fwd_varlen``, ``fwd_dropout``, ``bwd`` and
+``qkv_proj`` are convenience wrappers that allocate the outputs with torch and call them.  The
 shared library is loaded on first use and a missing or unloadable library
 raises -- there is no fallback path.
 """
@@ -18,6 +18,7 @@ from ._lib import (  # noqa: F401
     fa_fwd_dropout,
     fa_fwd_fp8,
     fa_fwd_varlen,
+    fa_qkv_proj,
     fa_strerror,
     fa_version,
     fwd,
@@ -25,4 +26,5 @@ from ._lib import (  # noqa: F401
     fwd_varlen,
     library_path,
     load,
+    qkv_proj,
 )

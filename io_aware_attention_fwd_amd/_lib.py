@@ -1,9 +1,10 @@
 """ctypes binding of libfa.so: argument marshalling only.
 
 ``fa_fwd``, ``fa_fwd_fp8``, ``fa_fwd_varlen``, ``fa_fwd_dropout``, ``fa_bwd``,
-``fa_strerror`` and ``fa_version`` take the same arguments as the C functions
-declared in ``include/fa.h`` (device pointers as Python ints, the stream as a
-``hipStream_t`` int or None).  ``fwd``, ``fwd_varlen``, ``fwd_dropout`` and ``bwd`` allocate
+``fa_qkv_proj``, ``fa_strerror`` and ``fa_version`` take the same arguments as
+the C functions declared in ``include/fa.h`` (device pointers as Python ints,
+the stream as a ``hipStream_t`` int or None).  ``fwd``, ``fwd_varlen``,
+``fwd_dropout``, ``bwd`` and ``qkv_proj`` allocate
 their outputs (and the backward workspace) with torch on the inputs' device
 and call the library on torch's current stream.  Every step of the computation runs
 in the library's HIP kernels; if the library is missing or fails to load, the
@@ -57,6 +58,8 @@ def load() -> ctypes.CDLL:
     lib.fa_fwd_dropout.restype = ci
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, cf, ci, ci, vp]
     lib.fa_bwd.restype = ci
+    lib.fa_qkv_proj.argtypes = [vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, vp]
+    lib.fa_qkv_proj.restype = ci
     lib.fa_strerror.argtypes = [ci]
     lib.fa_strerror.restype = ctypes.c_char_p
     lib.fa_version.argtypes = []
@@ -84,6 +87,10 @@ def fa_fwd_dropout(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, p_drop, se
 
 def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, scale, causal, dtype, stream) -> int:
     return load().fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, scale, int(causal), dtype, stream)
+
+
+def fa_qkv_proj(x, w, bias, q, k, v, B, N, D, H, d, dtype, stream) -> int:
+    return load().fa_qkv_proj(x, w, bias, q, k, v, B, N, D, H, d, dtype, stream)
 
 
 def fa_strerror(code: int) -> str:
@@ -220,3 +227,24 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse:
     if rc != 0:
         raise FaError(rc, "fa_bwd")
     return dq, dk, dv
+
+
+def qkv_proj(x: torch.Tensor, w: torch.Tensor, bias: torch.Tensor | None, H: int, d: int, *,
+             stream: torch.cuda.Stream | None = None):
+    """Fused QKV projection: x [B, N, D], w [3 H d, D], bias [3 H d] or None
+    (binary16 or bfloat16 device tensors); returns (Q, K, V), each [B, H, N, d]."""
+    if x.dtype not in (torch.float16, torch.bfloat16) or w.dtype != x.dtype or (bias is not None and bias.dtype != x.dtype):
+        raise TypeError("x, w and bias must share one 16-bit dtype")
+    if x.dim() != 3 or w.shape != (3 * H * d, x.shape[2]) or (bias is not None and bias.shape != (3 * H * d,)):
+        raise ValueError(f"shapes x {tuple(x.shape)}, w {tuple(w.shape)} do not match H={H}, d={d}")
+    if not (x.is_contiguous() and w.is_contiguous() and (bias is None or bias.is_contiguous())):
+        raise ValueError("x, w and bias must be contiguous")
+    B, N, D = x.shape
+    q, k, v = (torch.empty((B, H, N, d), dtype=x.dtype, device=x.device) for _ in range(3))
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device)
+    rc = fa_qkv_proj(x.data_ptr(), w.data_ptr(), None if bias is None else bias.data_ptr(), q.data_ptr(),
+                     k.data_ptr(), v.data_ptr(), B, N, D, H, d, _TORCH_DTYPES[x.dtype], stream.cuda_stream)
+    if rc != 0:
+        raise FaError(rc, "fa_qkv_proj")
+    return q, k, v

@@ -172,6 +172,53 @@ int backward(const void* q, const void* k, const void* v, const void* o, const f
   return FA_OK;
 }
 
+int qkv_proj(const void* x, const void* w, const void* bias, void* q, void* k, void* v, int B, int N, int D, int H,
+             int d, int dtype, void* stream) {
+  if (!x || !w || !q || !k || !v) return FA_ERR_NULL_PTR;
+  if (B < 1 || N < 1 || H < 1 || D < 64 || D % 64 != 0) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+  if (dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
+  const int64_t M = (int64_t)B * N, ncol = (int64_t)3 * H * d;
+  // X and W are addressed with 32-bit byte offsets, and the grid must fit an int
+  // (a tile's 128 rows included: its loads use 32-bit offsets too)
+  if (M * D * 2 >= ((int64_t)1 << 31) || ncol * D * 2 >= ((int64_t)1 << 31) || (int64_t)128 * D * 2 >= ((int64_t)1 << 31))
+    return FA_ERR_SHAPE;
+  const int64_t n_ftiles = (ncol + 127) / 128, total_wg = n_ftiles * ((M + 127) / 128);
+  if (total_wg >= ((int64_t)1 << 31)) return FA_ERR_SHAPE;
+  if (!aligned(x, 16) || !aligned(w, 16) || !aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) ||
+      (bias && !aligned(bias, 8)))
+    return FA_ERR_ALIGN;
+  const size_t x_sz = (size_t)M * D * 2, w_sz = (size_t)ncol * D * 2, b_sz = bias ? (size_t)ncol * 2 : 0;
+  const size_t o_sz = (size_t)M * H * d * 2;
+  const void* ins[3] = {x, w, bias};
+  const size_t in_sz[3] = {x_sz, w_sz, b_sz};
+  void* outs[3] = {q, k, v};
+  for (int i = 0; i < 3; ++i) {
+    for (int j = 0; j < 3; ++j)
+      if (in_sz[j] && overlap(outs[i], o_sz, ins[j], in_sz[j])) return FA_ERR_ALIAS;
+    for (int j = i + 1; j < 3; ++j)
+      if (overlap(outs[i], o_sz, outs[j], o_sz)) return FA_ERR_ALIAS;
+  }
+  fa::ProjParams p;
+  p.x = x;
+  p.w = w;
+  p.bias = bias;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.M = (int)M;
+  p.N = N;
+  p.D = D;
+  p.H = H;
+  p.d = d;
+  p.Ncol = (int)ncol;
+  p.n_ftiles = (int)n_ftiles;
+  p.total_wg = (int)total_wg;
+  if (fa::launch_qkv_proj(static_cast<fa::Dtype>(dtype), p, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return FA_ERR_HIP;
+  return FA_OK;
+}
+
 bool known_dtype(int dtype) { return dtype == FA_DTYPE_F16 || dtype == FA_DTYPE_BF16 || dtype == FA_DTYPE_FP8_E4M3; }
 
 }  // namespace
@@ -222,6 +269,11 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
            void* dk, void* dv, float* delta, int B, int H, int N, int d, float scale, int causal, int dtype,
            void* stream) {
   return backward(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, scale, causal, dtype, stream);
+}
+
+int fa_qkv_proj(const void* x, const void* w, const void* bias, void* q, void* k, void* v, int B, int N, int D, int H,
+                int d, int dtype, void* stream) {
+  return qkv_proj(x, w, bias, q, k, v, B, N, D, H, d, dtype, stream);
 }
 
 const char* fa_strerror(int code) {

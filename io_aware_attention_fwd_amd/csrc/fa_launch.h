@@ -59,6 +59,19 @@ struct BwdParams {
   float scale;   // multiplies dQ and dK at the end
 };
 
+// Fused QKV projection: Y = X W^T + bias written as Q, K, V in [B, H, N, d].
+struct ProjParams {
+  const void* x;     // [M, D] tokens, M = B * N
+  const void* w;     // [Ncol, D] weight, Ncol = 3 * H * d
+  const void* bias;  // [Ncol] or nullptr
+  void* q;
+  void* k;
+  void* v;
+  int M, N, D, H, d, Ncol;
+  int n_ftiles;  // ceil(Ncol / 128)
+  int total_wg;  // n_ftiles * ceil(M / 128)
+};
+
 enum class Dtype { F16 = 0, BF16 = 1, FP8 = 2 };
 
 // Rows of Q one workgroup owns for the instance chosen for this call (sizes the grid).
@@ -66,6 +79,9 @@ int rows_per_workgroup(Dtype dt, int d, bool causal, int N, bool dropout);
 
 // Enqueue one forward pass; returns hipSuccess or the launch error.
 hipError_t launch_fwd(Dtype dt, int d, bool causal, const FwdParams& p, hipStream_t stream);
+
+// Enqueue the fused QKV projection (16-bit types; D a multiple of 64).
+hipError_t launch_qkv_proj(Dtype dt, const ProjParams& p, hipStream_t stream);
 
 // Rows (queries for dQ, keys for dK/dV) one backward workgroup owns.
 constexpr int kBwdRows = 128;

@@ -40,8 +40,8 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     declared = _declared_functions()
-    assert declared == ["fa_bwd", "fa_fwd", "fa_fwd_dropout", "fa_fwd_fp8", "fa_fwd_varlen", "fa_strerror",
-                        "fa_version"]
+    assert declared == ["fa_bwd", "fa_fwd", "fa_fwd_dropout", "fa_fwd_fp8", "fa_fwd_varlen", "fa_qkv_proj",
+                        "fa_strerror", "fa_version"]
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.library_path()], capture_output=True, text=True, check=True).stdout
     exported = set(re.findall(r"\bT (fa_\w+)$", out, flags=re.M))
     for name in declared:
@@ -155,6 +155,35 @@ def _calld(p_drop=0.1, seed=1, offset=0, **kw):
 @no_gpu
 def test_fa_fwd_dropout_rejects(lib, p_drop, kw, code):
     assert _calld(p_drop, **kw) == _codes()[code]
+
+
+def _callp(**kw):
+    a = dict(x=BASE, w=BASE + SPAN, bias=BASE + 2 * SPAN, q=BASE + 3 * SPAN, k=BASE + 4 * SPAN, v=BASE + 5 * SPAN,
+             B=2, N=100, D=256, H=4, d=64, dtype=_lib.FA_DTYPE_BF16, stream=None)
+    a.update(kw)
+    return _lib.fa_qkv_proj(a["x"], a["w"], a["bias"], a["q"], a["k"], a["v"], a["B"], a["N"], a["D"], a["H"], a["d"],
+                            a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("case,kw,code", [
+    ("null x", dict(x=None), "FA_ERR_NULL_PTR"),
+    ("null v", dict(v=None), "FA_ERR_NULL_PTR"),
+    ("N=0", dict(N=0), "FA_ERR_SHAPE"),
+    ("D=96", dict(D=96), "FA_ERR_SHAPE"),
+    ("D=0", dict(D=0), "FA_ERR_SHAPE"),
+    ("X of 2 GiB", dict(B=1, N=1 << 14, D=1 << 16), "FA_ERR_SHAPE"),
+    ("d=32", dict(d=32), "FA_ERR_HEADDIM"),
+    ("fp8", dict(dtype=_lib.FA_DTYPE_FP8_E4M3), "FA_ERR_DTYPE"),
+    ("x misaligned", dict(x=BASE + 2), "FA_ERR_ALIGN"),
+    ("bias misaligned", dict(bias=BASE + 2 * SPAN + 4), "FA_ERR_ALIGN"),
+    ("q is x", dict(q=BASE), "FA_ERR_ALIAS"),
+    ("k inside w", dict(k=BASE + SPAN + 1024), "FA_ERR_ALIAS"),
+    ("v overlaps q", dict(v=BASE + 3 * SPAN + 4096), "FA_ERR_ALIAS"),
+    ("q on the bias", dict(q=BASE + 2 * SPAN), "FA_ERR_ALIAS"),
+])
+@no_gpu
+def test_fa_qkv_proj_rejects(lib, case, kw, code):
+    assert _callp(**kw) == _codes()[code], case
 
 
 def _callv(**kw):
