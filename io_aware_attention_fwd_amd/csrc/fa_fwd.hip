@@ -67,6 +67,12 @@ struct Shape {
   static constexpr int kSV = kGranV * 16;                   // bytes per V stage
   static constexpr int kBlkK = (kGranK + 63) / 64;  // direct-load instructions (64 granules each) per K stage
   static constexpr int kBlkV = (kGranV + 63) / 64;
+  // Stage allocations are whole direct-load blocks, so the lanes of a partial
+  // last block write into the stage's own tail.
+  static constexpr int kAllocK = kBlkK * 1024;
+  static constexpr int kAllocV = kBlkV * 1024;
+  static constexpr int kJK = (kBlkK + NW - 1) / NW;  // direct loads per wave per K stage (at most)
+  static constexpr int kJV = (kBlkV + NW - 1) / NW;
   static constexpr int kQSteps = Tr::kFp8 ? D / 64 : D / 16;  // QK instructions per 32x32 block
   static constexpr int kKReads = kKB * kQSteps * (Tr::kFp8 ? 2 : 1);  // 128-bit LDS reads of K per tile
   static constexpr int kQKMfma = kKB * kQSteps * kQB;                 // Q K^T instructions per tile
@@ -90,10 +96,10 @@ __global__ __launch_bounds__(NW * 64, WPE) void fa_fwd_kernel(FwdParams p) {
   // Two LDS stages.  Separate arrays let the compiler tell the
   // direct-to-LDS loads of one stage from the reads of the other (with one
   // array and computed offsets it waits for every load before any read).
-  __shared__ __attribute__((aligned(16))) char lds_k0[S::kSK];
-  __shared__ __attribute__((aligned(16))) char lds_k1[S::kSK];
-  __shared__ __attribute__((aligned(16))) char lds_v0[S::kSV];
-  __shared__ __attribute__((aligned(16))) char lds_v1[S::kSV];
+  __shared__ __attribute__((aligned(16))) char lds_k0[S::kAllocK];
+  __shared__ __attribute__((aligned(16))) char lds_k1[S::kAllocK];
+  __shared__ __attribute__((aligned(16))) char lds_v0[S::kAllocV];
+  __shared__ __attribute__((aligned(16))) char lds_v1[S::kAllocV];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -161,37 +167,50 @@ __global__ __launch_bounds__(NW * 64, WPE) void fa_fwd_kernel(FwdParams p) {
   const int n_kv = CAUSAL ? min(n_all, (q0 + S::kBR - 1) / BC + 1) : n_all;
 
   // ---- direct HBM -> LDS tile loads.  Lane L of direct-load instruction
-  // `blk` writes LDS granule 64*blk + L of the stage; it fetches the chunk of
-  // the tile that the layout places there, and pad granules (and granules past
-  // the stage) are left alone.  The per-lane source offsets are fixed for the
-  // whole kernel; only the tile's first key moves.
-  auto issue_k = [&](int kt, char* dk) __attribute__((always_inline)) {
-    const int k0 = kt * BC;
+  // `blk` writes LDS granule 64*blk + L of the stage and fetches the chunk of
+  // the tile that the layout places there.  Lanes whose granule is padding
+  // (or past the tile, in a partial last block) fetch a harmless in-bounds
+  // duplicate instead of being masked off, so a load is one instruction with
+  // no exec-mask branches.  The per-lane source offsets within a tile are
+  // computed once and the tile's offset is added per load; it stays in the
+  // per-lane offset (not the scalar one) because only that part is checked
+  // against the slice's range, which zero-fills the rows past N of the last
+  // tile.  The block index (uniform within the wave) is a scalar.
+  int koff[S::kJK], voff[S::kJV], kblk[S::kJK], vblk[S::kJV];
 #pragma unroll
-    for (int j = 0; j < (S::kBlkK + NW - 1) / NW; ++j) {
-      const int blk = wave + j * NW;
-      const int g = blk * 64 + lane;
-      const int r = g / S::kGK, c = g - r * S::kGK;
-      if (blk < S::kBlkK && g < S::kGranK && c < S::kCK) load_lds16(rk, dk + blk * 1024, (k0 + r) * rowb + c * 16);
-    }
+  for (int j = 0; j < S::kJK; ++j) {
+    kblk[j] = __builtin_amdgcn_readfirstlane(wave + j * NW);
+    const int g = (wave + j * NW) * 64 + lane;
+    const int r = g / S::kGK;
+    const int c = min(g - r * S::kGK, S::kCK - 1);  // the pad granule repeats the row's last chunk
+    koff[j] = r * rowb + c * 16;
+  }
+#pragma unroll
+  for (int j = 0; j < S::kJV; ++j) {
+    vblk[j] = __builtin_amdgcn_readfirstlane(wave + j * NW);
+    const int g = (wave + j * NW) * 64 + lane;
+    const int grp = g / S::kGV;
+    const int off = (g - grp * S::kGV) * 16;  // byte offset inside the group of rows
+    int r = grp * S::VL::kGroupRows, c = 0;    // pad granules repeat the group's first chunk
+#pragma unroll
+    for (int i = 0; i < S::VL::kGroupRows; ++i)
+      if (off >= S::VL::row(i) && off < S::VL::row(i) + S::kRV) {
+        r = grp * S::VL::kGroupRows + i;
+        c = (off - S::VL::row(i)) / 16;
+      }
+    voff[j] = r * rowb + c * 16;
+  }
+  auto issue_k = [&](int kt, char* dk) __attribute__((always_inline)) {
+    const int toff = kt * BC * rowb;
+#pragma unroll
+    for (int j = 0; j < S::kJK; ++j)
+      if (kblk[j] < S::kBlkK) load_lds16(rk, dk + kblk[j] * 1024, koff[j] + toff);
   };
   auto issue_v = [&](int kt, char* dv) __attribute__((always_inline)) {
-    const int k0 = kt * BC;
+    const int toff = kt * BC * rowb;
 #pragma unroll
-    for (int j = 0; j < (S::kBlkV + NW - 1) / NW; ++j) {
-      const int blk = wave + j * NW;
-      const int g = blk * 64 + lane;
-      const int grp = g / S::kGV;
-      const int off = (g - grp * S::kGV) * 16;  // byte offset inside the group of rows
-      int r = -1, c = 0;
-#pragma unroll
-      for (int i = 0; i < S::VL::kGroupRows; ++i)
-        if (off >= S::VL::row(i) && off < S::VL::row(i) + S::kRV) {
-          r = grp * S::VL::kGroupRows + i;
-          c = (off - S::VL::row(i)) / 16;
-        }
-      if (blk < S::kBlkV && g < S::kGranV && r >= 0) load_lds16(rv, dv + blk * 1024, (k0 + r) * rowb + c * 16);
-    }
+    for (int j = 0; j < S::kJV; ++j)
+      if (vblk[j] < S::kBlkV) load_lds16(rv, dv + vblk[j] * 1024, voff[j] + toff);
   };
 
   f32x16 oacc[S::kDB][S::kQB];
