@@ -268,8 +268,11 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(BwdParams p) {
 }
 
 // ------------------------------------------------------------ dK/dV kernel
-template <class Tr, int D, bool CAUSAL>
-__global__ __launch_bounds__(256, D == 64 ? 2 : 1) void fa_bwd_dkdv_kernel(BwdParams p) {
+// WPE: minimum waves per SIMD the registers are budgeted for (at d = 128, 2
+// fits the kernel into 256 registers; 1 leaves it more, for grids too small
+// to put two workgroups on a CU).
+template <class Tr, int D, bool CAUSAL, int WPE>
+__global__ __launch_bounds__(256, WPE) void fa_bwd_dkdv_kernel(BwdParams p) {
   constexpr int NW = 4, BQ = 32;
   constexpr bool kBf = Tr::kPvBf16;
   using B = BwdShape<D>;
@@ -341,40 +344,38 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void fa_bwd_dkdv_kernel(BwdPa
       const u32x4 da = lds_read_b128(tdo, rbase + 32 * st);
       dp = mfma16(da, v16[st], dp, kBf);
     }
-    // element r of the accumulators belongs to query row 8*(r/4) + 4*half + r%4 of the tile
-    float L[16], Dr[16];
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      // (whole-vector casts: a bit cast of a vector element subscript reads
-      // element 0 whatever the index)
-      const f32x4 l4 = __builtin_bit_cast(f32x4, lds_read_b128((const char*)tld, (8 * g + 4 * half) * 4));
-      const f32x4 d4 = __builtin_bit_cast(f32x4, lds_read_b128((const char*)tld, (BQ + 8 * g + 4 * half) * 4));
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        L[4 * g + e] = l4[e] * kLog2e;
-        Dr[4 * g + e] = d4[e];
-      }
-    }
+    // Element r of the accumulators belongs to query row 8*(r/4) + 4*half +
+    // r%4 of the tile; the four rows of group r/4 take their lse and D from
+    // one 128-bit LDS read each, right where they are used.  (Whole-vector
+    // casts: a bit cast of a vector element subscript reads element 0
+    // whatever the index.)
     const bool need_mask = (qb0 + BQ > N) || (CAUSAL && qb0 < kw0 + 31);
     u32x4 pp[2], pds[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float pr[2], ds[2];
+      for (int eh = 0; eh < 2; ++eh) {
+        const int g = 2 * t + eh;
+        const f32x4 l4 = __builtin_bit_cast(f32x4, lds_read_b128((const char*)tld, (8 * g + 4 * half) * 4));
+        const f32x4 d4 = __builtin_bit_cast(f32x4, lds_read_b128((const char*)tld, (BQ + 8 * g + 4 * half) * 4));
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int r = 8 * t + 2 * e + j;
-          float x = __builtin_fmaf(s[r], c, -L[r]);
-          if (need_mask) {
-            const int query = qb0 + 8 * (r >> 2) + 4 * half + (r & 3);
-            if (query >= N || (CAUSAL && key > query)) x = -INFINITY;
+        for (int el = 0; el < 2; ++el) {
+          const int e = 2 * eh + el;
+          float pr[2], ds[2];
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const int r = 8 * t + 2 * e + j;  // = 4 * g + 2 * el + j
+            float x = __builtin_fmaf(s[r], c, -l4[2 * el + j] * kLog2e);
+            if (need_mask) {
+              const int query = qb0 + 8 * (r >> 2) + 4 * half + (r & 3);
+              if (query >= N || (CAUSAL && key > query)) x = -INFINITY;
+            }
+            pr[j] = __builtin_amdgcn_exp2f(x);
+            ds[j] = pr[j] * (dp[r] - d4[2 * el + j]);
           }
-          pr[j] = __builtin_amdgcn_exp2f(x);
-          ds[j] = pr[j] * (dp[r] - Dr[r]);
+          pp[t][e] = pack_p<kBf>(pr[0], pr[1]);
+          pds[t][e] = pack_p<kBf>(ds[0], ds[1]);
         }
-        pp[t][e] = pack_p<kBf>(pr[0], pr[1]);
-        pds[t][e] = pack_p<kBf>(ds[0], ds[1]);
       }
 #pragma unroll
     for (int db = 0; db < B::kDB; ++db)
@@ -412,7 +413,16 @@ hipError_t launch_bwd_typed(const BwdParams& p, hipStream_t stream) {
   hipLaunchKernelGGL((fa_bwd_dq_kernel<Tr, D, CAUSAL>), dim3(p.total_wg), dim3(256), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<Tr, D, CAUSAL>), dim3(p.total_wg), dim3(256), 0, stream, p);
+  // (256 CUs: at d = 128 two waves per SIMD pay off once there are two
+  // workgroups per CU; at d = 64 the kernel fits two with room to spare)
+  if constexpr (D == 64) {
+    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<Tr, D, CAUSAL, 2>), dim3(p.total_wg), dim3(256), 0, stream, p);
+  } else {
+    if (p.total_wg >= 512)
+      hipLaunchKernelGGL((fa_bwd_dkdv_kernel<Tr, D, CAUSAL, 2>), dim3(p.total_wg), dim3(256), 0, stream, p);
+    else
+      hipLaunchKernelGGL((fa_bwd_dkdv_kernel<Tr, D, CAUSAL, 1>), dim3(p.total_wg), dim3(256), 0, stream, p);
+  }
   return hipGetLastError();
 }
 
