@@ -645,14 +645,14 @@ constexpr Variant kVariants[] = {{32, 8, 64, 1, 2}, {32, 4, 64, 0, 4}, {32, 4, 6
                                  {64, 4, 64, 0, 2}};
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
-// Measured on MI355X (A/B in one process): the ping-pong schedule wins at
-// d = 128 for 16-bit types (fp8, with half the operand bytes, prefers the
-// plain schedule at three waves per SIMD); at d = 64 the plain schedule, with
-// 64 rows per wave for long non-causal sequences and 32 rows per wave at
-// three waves per SIMD otherwise.
+// Measured on MI355X (tile sweep under rocprofv3): the ping-pong schedule
+// wins at d = 128 for 16-bit types (fp8, with half the operand bytes,
+// prefers the plain schedule at two waves per SIMD); at d = 64 the plain
+// schedule, with 64 rows per wave for non-causal sequences of 1024 rows or
+// more and 32 rows per wave at three waves per SIMD otherwise.
 int default_variant(Dtype dt, int d, bool causal, int N) {
-  if (d == 128) return dt == Dtype::FP8 ? 2 : 0;  // plain at three waves per SIMD for fp8, else ping-pong
-  if (!causal && N >= 2048) return 4;     // 64 rows per wave: half the LDS operand traffic per FLOP
+  if (d == 128) return dt == Dtype::FP8 ? 3 : 0;  // plain at two waves per SIMD for fp8, else ping-pong
+  if (!causal && N >= 1024) return 4;     // 64 rows per wave: half the LDS operand traffic per FLOP
   return 2;                               // plain, three waves per SIMD
 }
 
