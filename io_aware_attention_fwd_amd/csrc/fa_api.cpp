@@ -180,10 +180,13 @@ int qkv_proj(const void* x, const void* w, const void* bias, void* q, void* k, v
   if (dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
   const int64_t M = (int64_t)B * N, ncol = (int64_t)3 * H * d;
   // X and W are addressed with 32-bit byte offsets, and the grid must fit an int
-  // (a tile's 128 rows included: its loads use 32-bit offsets too)
-  if (M * D * 2 >= ((int64_t)1 << 31) || ncol * D * 2 >= ((int64_t)1 << 31) || (int64_t)128 * D * 2 >= ((int64_t)1 << 31))
+  // (a tile's rows included: its loads use 32-bit offsets too)
+  const fa::ProjTiling tl = fa::proj_tiling(M, ncol);
+  const int64_t tile_rows = tl.tokens > tl.features ? tl.tokens : tl.features;
+  if (M * D * 2 >= ((int64_t)1 << 31) || ncol * D * 2 >= ((int64_t)1 << 31) || tile_rows * D * 2 >= ((int64_t)1 << 31))
     return FA_ERR_SHAPE;
-  const int64_t n_ftiles = (ncol + 127) / 128, total_wg = n_ftiles * ((M + 127) / 128);
+  const int64_t n_ftiles = (ncol + tl.features - 1) / tl.features;
+  const int64_t total_wg = n_ftiles * ((M + tl.tokens - 1) / tl.tokens);
   if (total_wg >= ((int64_t)1 << 31)) return FA_ERR_SHAPE;
   if (!aligned(x, 16) || !aligned(w, 16) || !aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) ||
       (bias && !aligned(bias, 8)))
@@ -212,6 +215,7 @@ int qkv_proj(const void* x, const void* w, const void* bias, void* q, void* k, v
   p.H = H;
   p.d = d;
   p.Ncol = (int)ncol;
+  p.tiling = tl.index;
   p.n_ftiles = (int)n_ftiles;
   p.total_wg = (int)total_wg;
   if (fa::launch_qkv_proj(static_cast<fa::Dtype>(dtype), p, static_cast<hipStream_t>(stream)) != hipSuccess)

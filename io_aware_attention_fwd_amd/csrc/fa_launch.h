@@ -68,9 +68,16 @@ struct ProjParams {
   void* k;
   void* v;
   int M, N, D, H, d, Ncol;
-  int n_ftiles;  // ceil(Ncol / 128)
-  int total_wg;  // n_ftiles * ceil(M / 128)
+  int tiling;    // which compiled tile (from proj_tiling)
+  int n_ftiles;  // ceil(Ncol / tile features)
+  int total_wg;  // n_ftiles * ceil(M / tile tokens)
 };
+
+// The QKV projection's tile for an M x Ncol product: an index and its size.
+struct ProjTiling {
+  int index, features, tokens;
+};
+ProjTiling proj_tiling(int64_t M, int64_t ncol);
 
 enum class Dtype { F16 = 0, BF16 = 1, FP8 = 2 };
 

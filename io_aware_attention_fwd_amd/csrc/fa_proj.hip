@@ -18,9 +18,13 @@
 // columns c of one head, which the epilogue writes as one 8-byte store into
 // the [B, H, N, d] output.
 //
-// Workgroup: 4 waves as 2 (features) x 2 (tokens), 64 x 64 outputs per wave,
-// a 128 x 128 tile per workgroup; k advances 64 at a time through two LDS
-// stages.
+// Workgroup: NWF x NWT waves (features x tokens), each owning 64 features x
+// WT tokens; k advances 64 at a time through two LDS stages.  Two shapes
+// are compiled: 4 waves of 64 x 64 (a 128 x 128 tile, two workgroups per
+// CU) and 8 waves of 64 x 128 (a 256 x 256 tile, one workgroup per CU).  The
+// larger tile halves the bytes each FLOP pulls from L2 into LDS, which is
+// what bounds large products; it is used when the grid still has at least
+// four workgroups per CU.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -30,73 +34,86 @@
 namespace fa {
 namespace {
 
-constexpr int kPT = 128;               // features (and tokens) per workgroup tile
 constexpr int kPK = 64;                // k per stage
 constexpr int kPRow = kPK * 2;         // bytes of one tile row per stage
 constexpr int kPRS = kPRow + 16;       // padded LDS row (one pad granule)
 constexpr int kPGR = kPRow / 16 + 1;   // LDS granules per padded row
-constexpr int kPGran = kPT * kPGR;     // granules per tile
-constexpr int kPBlk = (kPGran + 63) / 64;  // direct-load instructions per tile
-constexpr int kPStage = kPT * kPRS;    // bytes per tile per stage
+
+template <int NWF, int NWT, int WT>
+struct ProjTile {
+  static constexpr int kNW = NWF * NWT;             // waves per workgroup
+  static constexpr int kTB = WT / 32;               // 32-token blocks per wave
+  static constexpr int kTF = NWF * 64;              // features per tile
+  static constexpr int kTT = NWT * WT;              // tokens per tile
+  static constexpr int kBlkW = (kTF * kPGR + 63) / 64;  // direct-load instructions per stage
+  static constexpr int kBlkX = (kTT * kPGR + 63) / 64;
+  static constexpr int kStW = kBlkW * 1024;         // whole blocks: a partial last block
+  static constexpr int kStX = kBlkX * 1024;         // writes into the stage's own tail
+};
+using TileSmall = ProjTile<2, 2, 64>;   // 128 x 128, 4 waves
+using TileLarge = ProjTile<4, 2, 128>;  // 256 x 256, 8 waves
 
 }  // namespace
 
-template <bool BF16>
-__global__ __launch_bounds__(256, 2) void fa_qkv_proj_kernel(ProjParams p) {
-  __shared__ __attribute__((aligned(16))) char lw0[kPStage];
-  __shared__ __attribute__((aligned(16))) char lw1[kPStage];
-  __shared__ __attribute__((aligned(16))) char lx0[kPStage];
-  __shared__ __attribute__((aligned(16))) char lx1[kPStage];
+template <bool BF16, int NWF, int NWT, int WT>
+__global__ __launch_bounds__(NWF * NWT * 64, 8 / (NWF * NWT)) void fa_qkv_proj_kernel(ProjParams p) {
+  using T = ProjTile<NWF, NWT, WT>;
+  __shared__ __attribute__((aligned(16))) char lw0[T::kStW];
+  __shared__ __attribute__((aligned(16))) char lw1[T::kStW];
+  __shared__ __attribute__((aligned(16))) char lx0[T::kStX];
+  __shared__ __attribute__((aligned(16))) char lx1[T::kStX];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, half = lane >> 5, l32 = lane & 31;
   const int tile = xcd_remap(blockIdx.x, p.total_wg);
   const int ft = tile % p.n_ftiles, tt = tile / p.n_ftiles;  // consecutive tiles share the token block
-  const int f0 = ft * kPT, t0 = tt * kPT;
-  const int wf = (wave & 1) * 64, wt = (wave >> 1) * 64;    // the wave's 64 x 64 corner
+  const int f0 = ft * T::kTF, t0 = tt * T::kTT;
+  const int wf = (wave % NWF) * 64, wt = (wave / NWF) * WT;  // the wave's corner
 
   const u32 rowb = (u32)p.D * 2;
-  const auto rw = make_rsrc((const char*)p.w + (size_t)f0 * rowb, (u32)(min(kPT, p.Ncol - f0)) * rowb);
-  const auto rx = make_rsrc((const char*)p.x + (size_t)t0 * rowb, (u32)(min(kPT, p.M - t0)) * rowb);
+  const auto rw = make_rsrc((const char*)p.w + (size_t)f0 * rowb, (u32)(min(T::kTF, p.Ncol - f0)) * rowb);
+  const auto rx = make_rsrc((const char*)p.x + (size_t)t0 * rowb, (u32)(min(T::kTT, p.M - t0)) * rowb);
 
   // Lane L of direct-load instruction blk fills granule 64*blk + L of the
-  // padded tile: row g / kPGR, chunk g % kPGR (chunk kPGR-1 is the pad).
+  // padded tile: row g / kPGR, chunk g % kPGR.  The pad chunk (and lanes of
+  // a partial last block) load an in-bounds duplicate rather than being
+  // masked off; rows past the matrix read as zero (range-checked).
+  auto load_blk = [&](__amdgpu_buffer_rsrc_t rs, char* dst, int blk, int kbyte) __attribute__((always_inline)) {
+    const int g = blk * 64 + lane;
+    const int r = g / kPGR, c = min(g - r * kPGR, kPGR - 2);
+    load_lds16(rs, dst + blk * 1024, r * (int)rowb + kbyte + c * 16);
+  };
   auto issue = [&](int kk, char* dw, char* dx) __attribute__((always_inline)) {
     const int kbyte = kk * kPRow;
 #pragma unroll
-    for (int j = 0; j < (kPBlk + 3) / 4; ++j) {
-      const int blk = wave + 4 * j;
-      const int g = blk * 64 + lane;
-      const int r = g / kPGR, c = g - r * kPGR;
-      if (blk < kPBlk && g < kPGran && c < kPGR - 1) {
-        load_lds16(rw, dw + blk * 1024, r * (int)rowb + kbyte + c * 16);
-        load_lds16(rx, dx + blk * 1024, r * (int)rowb + kbyte + c * 16);
-      }
-    }
+    for (int j = 0; j < (T::kBlkW + T::kNW - 1) / T::kNW; ++j)
+      if (wave + T::kNW * j < T::kBlkW) load_blk(rw, dw, wave + T::kNW * j, kbyte);
+#pragma unroll
+    for (int j = 0; j < (T::kBlkX + T::kNW - 1) / T::kNW; ++j)
+      if (wave + T::kNW * j < T::kBlkX) load_blk(rx, dx, wave + T::kNW * j, kbyte);
   };
 
-  f32x16 acc[2][2];
+  f32x16 acc[2][T::kTB];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < T::kTB; ++j) acc[i][j] = f32x16{};
   const int abase = (wf + l32) * kPRS + 16 * half;  // W row of feature block 0 of the wave
   const int bbase = (wt + l32) * kPRS + 16 * half;  // X row of token block 0 of the wave
 
+  // One matrix k-step reads 2 W and kTB X operands for 2 x kTB instructions.
   auto step = [&](const char* tw, const char* tx) __attribute__((always_inline)) {
-    u32x4 a[2][kPK / 16], b[2][kPK / 16];
 #pragma unroll
-    for (int s = 0; s < kPK / 16; ++s)
+    for (int s = 0; s < kPK / 16; ++s) {
+      u32x4 a[2], b[T::kTB];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        a[i][s] = lds_read_b128(tw, abase + 32 * i * kPRS + 32 * s);
-        b[i][s] = lds_read_b128(tx, bbase + 32 * i * kPRS + 32 * s);
-      }
+      for (int i = 0; i < 2; ++i) a[i] = lds_read_b128(tw, abase + 32 * i * kPRS + 32 * s);
 #pragma unroll
-    for (int s = 0; s < kPK / 16; ++s)
+      for (int j = 0; j < T::kTB; ++j) b[j] = lds_read_b128(tx, bbase + 32 * j * kPRS + 32 * s);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma16(a[i][s], b[j][s], acc[i][j], BF16);
+        for (int j = 0; j < T::kTB; ++j) acc[i][j] = mfma16(a[i], b[j], acc[i][j], BF16);
+    }
   };
 
   const int nk = p.D / kPK;
@@ -141,7 +158,7 @@ __global__ __launch_bounds__(256, 2) void fa_qkv_proj_kernel(ProjParams p) {
       }
       char* outs = (char*)(s == 0 ? p.q : s == 1 ? p.k : p.v);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      for (int j = 0; j < T::kTB; ++j) {
         const int m = t0 + wt + 32 * j + l32;  // token
         if (m >= p.M) continue;
         const int b = m / p.N, n = m - b * p.N;
@@ -154,13 +171,40 @@ __global__ __launch_bounds__(256, 2) void fa_qkv_proj_kernel(ProjParams p) {
   }
 }
 
+namespace {
+
+template <class T>
+int64_t grid_of(int64_t M, int64_t ncol) {
+  return ((ncol + T::kTF - 1) / T::kTF) * ((M + T::kTT - 1) / T::kTT);
+}
+
+template <bool BF16, class T, int NWF, int NWT, int WT>
+void launch_tile(const ProjParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL((fa_qkv_proj_kernel<BF16, NWF, NWT, WT>), dim3(p.total_wg), dim3(T::kNW * 64), 0, stream, p);
+}
+
+}  // namespace
+
+ProjTiling proj_tiling(int64_t M, int64_t ncol) {
+  // 256 CUs: the large tile once its grid has at least four workgroups per CU
+  if (grid_of<TileLarge>(M, ncol) >= 4 * 256) return {1, TileLarge::kTF, TileLarge::kTT};
+  return {0, TileSmall::kTF, TileSmall::kTT};
+}
+
 hipError_t launch_qkv_proj(Dtype dt, const ProjParams& p, hipStream_t stream) {
-  if (dt == Dtype::F16)
-    hipLaunchKernelGGL((fa_qkv_proj_kernel<false>), dim3(p.total_wg), dim3(256), 0, stream, p);
-  else if (dt == Dtype::BF16)
-    hipLaunchKernelGGL((fa_qkv_proj_kernel<true>), dim3(p.total_wg), dim3(256), 0, stream, p);
-  else
-    return hipErrorInvalidValue;
+  if (dt != Dtype::F16 && dt != Dtype::BF16) return hipErrorInvalidValue;
+  const bool bf = dt == Dtype::BF16;
+  if (p.tiling == 1) {
+    if (bf)
+      launch_tile<true, TileLarge, 4, 2, 128>(p, stream);
+    else
+      launch_tile<false, TileLarge, 4, 2, 128>(p, stream);
+  } else {
+    if (bf)
+      launch_tile<true, TileSmall, 2, 2, 64>(p, stream);
+    else
+      launch_tile<false, TileSmall, 2, 2, 64>(p, stream);
+  }
   return hipGetLastError();
 }
 

@@ -121,3 +121,19 @@ def test_projection_then_attention(dtype, causal):
     dl = (np.abs(lse.cpu().numpy() - lse_ref) / np.maximum(1.0, np.abs(lse_ref))).max()
     print(f"[proj] end to end max|dO| {do:.3g}, max rel dlse {dl:.3g}")
     assert do <= gu.O_TOL[dtype] and dl <= gu.LSE_TOL
+
+
+def test_projection_large_tile_sampled():
+    """A product large enough for the 256 x 256 tile (at least four
+    workgroups per CU), with a partial token tile (M = 16000) and a partial
+    feature tile (3 H d = 5760); every feature of 320 sampled tokens,
+    including the first and last ones, against the oracle."""
+    B, N, D, H, d, dtype = 4, 4000, 1024, 30, 64, "bf16"
+    print(f"[proj] large tile B={B} N={N} D={D} H={H} d={d} {dtype}", flush=True)
+    pi = gen.make_projection(B, N, D, H, d, dtype, seed=5)
+    outs = _run(pi)
+    rng = np.random.default_rng(6)
+    toks = np.unique(np.concatenate([[0, 1, 255, 256, N - 1], rng.integers(0, N, 315)]))
+    sub = gen.ProjectionInputs(dtype, np.ascontiguousarray(pi.x[:, toks]), pi.w, pi.bias, H, d)
+    worst = _check(sub, [o[:, :, toks] for o in outs])
+    print(f"[proj] worst error / bar {worst:.3g} over {len(toks)} tokens per batch")
