@@ -17,6 +17,12 @@ memory clock levels in use under load, the fraction of the dense
 fp16 matrix-core peak, HBM traffic from committed rocprofv3 counters when they
 were taken on the current kernel source, and the CPU oracle timed on a bounded
 sample of the same workload.
+
+Other modes print one line each for the other entry points instead of the
+headline: ``--shape`` (another dense forward shape), ``--varlen`` (packed
+sequences), ``--dropout``, ``--bwd`` (the backward pass) and ``--proj`` (the
+fused QKV projection); ``--copy-calib-mib`` adds a plain device copy used to
+calibrate the HBM counters.
 """
 from __future__ import annotations
 
@@ -239,7 +245,8 @@ def cpu_baseline_varlen(x, cu, causal, scale, budget_s):
 
 
 def cpu_baseline(x, causal, scale, budget_s):
-    """The float64 oracle on as many (b, h) slices of ``x`` as fit in ``budget_s`` seconds."""
+    """The float64 oracle on the (b, h) slices of ``x``, cycling through them
+    until ``budget_s`` seconds have passed (or one pass, if that takes longer)."""
     import oracle
 
     B, H, N, d = x.shape
@@ -252,19 +259,20 @@ def cpu_baseline(x, causal, scale, budget_s):
         cores = None
     done, t0 = 0, time.perf_counter()
     while True:
-        b, h = divmod(done, H)
+        b, h = divmod(done % (B * H), H)
         qkv = [oracle.dequantize(a[b, h], dtype, x.descale[n]) for a, n in ((x.q, "q"), (x.k, "k"), (x.v, "v"))]
         oracle.attention_slice(qkv[0], qkv[1], qkv[2], scale, causal)
         done += 1
         el = time.perf_counter() - t0
-        if el >= budget_s or done >= B * H:
+        if el >= budget_s:
             break
     per_slice = el / done
     full_s = per_slice * B * H
     tflops = flops(B, H, N, d, causal) / full_s / 1e12
     return {"value": tflops, "unit": "TFLOPS", "cores": cores, "kind": "oracle",
-            "sample": f"{done} of {B * H} (b,h) slices of N={N}, d={d} ({dtype} inputs, float64 math) timed in "
-                      f"{el:.1f} s; full workload extrapolated to {full_s:.1f} s ({full_s * 1e3:.0f} ms per step)"}
+            "sample": f"{done} slice evaluations ({done / (B * H):.2f} passes over the {B * H} (b,h) slices) of N={N}, "
+                      f"d={d} ({dtype} inputs, float64 math) in {el:.1f} s; one full workload = {full_s:.2f} s "
+                      f"({full_s * 1e3:.0f} ms per step)"}
 
 
 def load_traffic(_unused=None):
