@@ -579,15 +579,23 @@ __global__ __launch_bounds__(NW * 64, WPE) void fa_fwd_kernel(FwdParams p) {
         issue_v(kt + 1, vn);
       }
       if (active(kt)) {
-        load_k(kc);
-        mma_qk();
-        // All K operand reads go out before the first Q K^T instruction.
-        __builtin_amdgcn_sched_group_barrier(0x100, S::kKReads, 0);  // DS reads
-        __builtin_amdgcn_sched_group_barrier(0x008, S::kQKMfma, 0);  // matrix instructions
-        __builtin_amdgcn_sched_barrier(0);
-        load_v(vc);  // in flight during the softmax
-        softmax(kt);
-        mma_pv();
+        if constexpr (WPE >= 4) {
+          // Four waves per SIMD leave 128 registers: each operand is read
+          // right before its instruction, so few operand registers are live.
+          qk_interleaved(kc);
+          softmax(kt);
+          pv_interleaved(vc);
+        } else {
+          load_k(kc);
+          mma_qk();
+          // All K operand reads go out before the first Q K^T instruction.
+          __builtin_amdgcn_sched_group_barrier(0x100, S::kKReads, 0);  // DS reads
+          __builtin_amdgcn_sched_group_barrier(0x008, S::kQKMfma, 0);  // matrix instructions
+          __builtin_amdgcn_sched_barrier(0);
+          load_v(vc);  // in flight during the softmax
+          softmax(kt);
+          mma_pv();
+        }
       }
     };
     issue_k(0, lds_k0);
@@ -645,15 +653,17 @@ constexpr Variant kVariants[] = {{32, 8, 64, 1, 2}, {32, 4, 64, 0, 4}, {32, 4, 6
                                  {64, 4, 64, 0, 2}};
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
-// Measured on MI355X (tile sweep under rocprofv3): the ping-pong schedule
-// wins at d = 128 for 16-bit types (fp8, with half the operand bytes,
-// prefers the plain schedule at two waves per SIMD); at d = 64 the plain
-// schedule, with 64 rows per wave for non-causal sequences of 1024 rows or
-// more and 32 rows per wave at three waves per SIMD otherwise.
-int default_variant(Dtype dt, int d, bool causal, int N) {
+// Measured on MI355X (tile sweep under rocprofv3, A/B runs in one process):
+// the ping-pong schedule wins at d = 128 for 16-bit types (fp8, with half
+// the operand bytes, prefers the plain schedule at two waves per SIMD); at
+// d = 64 the plain schedule, with 64 rows per wave for non-causal sequences
+// of 1024 rows or more and otherwise 32 rows per wave at four waves per SIMD
+// (three for fp8, and with dropout, whose generator does not fit the
+// four-wave register budget).
+int default_variant(Dtype dt, int d, bool causal, int N, bool dropout) {
   if (d == 128) return dt == Dtype::FP8 ? 3 : 0;  // plain at two waves per SIMD for fp8, else ping-pong
   if (!causal && N >= 1024) return 4;     // 64 rows per wave: half the LDS operand traffic per FLOP
-  return 2;                               // plain, three waves per SIMD
+  return dt == Dtype::FP8 || dropout ? 2 : 1;  // plain, three or four waves per SIMD
 }
 
 int selected_variant(Dtype dt, int d, bool causal, int N, bool dropout) {
@@ -666,7 +676,7 @@ int selected_variant(Dtype dt, int d, bool causal, int N, bool dropout) {
             kVariants[i].sched == v.sched && kVariants[i].wpe == v.wpe)
           return i;
   }
-  return default_variant(dt, d, causal, N);
+  return default_variant(dt, d, causal, N, dropout);
 }
 
 template <class Tr, int D, bool CAUSAL>
