@@ -268,9 +268,9 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(BwdParams p) {
 }
 
 // ------------------------------------------------------------ dK/dV kernel
-// WPE: minimum waves per SIMD the registers are budgeted for (at d = 128, 2
-// fits the kernel into 256 registers; 1 leaves it more, for grids too small
-// to put two workgroups on a CU).
+// WPE: minimum waves per SIMD the registers are budgeted for (at d = 64, 3;
+// at d = 128, 2 fits the kernel into 256 registers and 1 leaves it more, for
+// grids too small to put two workgroups on a CU).
 template <class Tr, int D, bool CAUSAL, int WPE>
 __global__ __launch_bounds__(256, WPE) void fa_bwd_dkdv_kernel(BwdParams p) {
   constexpr int NW = 4, BQ = 32;
@@ -414,9 +414,10 @@ hipError_t launch_bwd_typed(const BwdParams& p, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // (256 CUs: at d = 128 two waves per SIMD pay off once there are two
-  // workgroups per CU; at d = 64 the kernel fits two with room to spare)
+  // workgroups per CU; at d = 64 the kernel fits three per SIMD, which is
+  // 9 % faster than two on causal B8 H32 N4096 and the same without mask)
   if constexpr (D == 64) {
-    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<Tr, D, CAUSAL, 2>), dim3(p.total_wg), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<Tr, D, CAUSAL, 3>), dim3(p.total_wg), dim3(256), 0, stream, p);
   } else {
     if (p.total_wg >= 512)
       hipLaunchKernelGGL((fa_bwd_dkdv_kernel<Tr, D, CAUSAL, 2>), dim3(p.total_wg), dim3(256), 0, stream, p);
