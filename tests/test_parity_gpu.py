@@ -156,3 +156,25 @@ def test_lse_self_consistency_large():
         w = np.exp(s - lse_np[b, h, rows][:, None])
         assert np.abs(w.sum(axis=1) - 1.0).max() < 1e-3
         assert np.abs(w @ v - o_np[b, h, rows]).max() < 1e-2
+
+
+@pytest.mark.parametrize("N,d,dtype,causal", [(131072, 128, "bf16", True), (65536, 64, "f16", False)])
+def test_long_sequences_sampled_rows(N, d, dtype, causal):
+    """Long sequences (a 32 MiB slice at N = 131072, d = 128): 24 sampled rows
+    per slice, the first and last included, each against the oracle on the
+    keys it sees (causal row i: keys 0..i as a plain attention problem)."""
+    B, H = 1, 2
+    print(f"[long] N={N} d={d} {dtype} causal={causal}", flush=True)
+    x = gen.make(B, H, N, d, dtype, seed=12)
+    scale = 1 / math.sqrt(d)
+    o, lse = gu.run_gpu(x, scale, causal)
+    o_np, lse_np = gu.o_to_numpy(o), lse.cpu().numpy().astype(np.float64)
+    rng = np.random.default_rng(13)
+    rows = np.unique(np.concatenate([[0, 1, 63, 64, N - 2, N - 1], rng.integers(0, N, 18)]))
+    for h in range(H):
+        q, k, v = gu.dequant(x, 0, h)
+        for i in rows:
+            n_vis = i + 1 if causal else N
+            o_ref, lse_ref = oracle.attention_slice(q[i:i + 1], k[:n_vis], v[:n_vis], scale, False)
+            assert np.abs(o_np[0, h, i] - o_ref[0]).max() <= gu.O_TOL[dtype], (h, i)
+            assert abs(lse_np[0, h, i] - lse_ref[0]) <= gu.LSE_TOL * max(1.0, abs(lse_ref[0])), (h, i)
