@@ -1,5 +1,8 @@
 /*
- * fa.h -- C ABI of libfa.so, the gfx950 (MI355X) FlashAttention forward pass.
+ * fa.h -- C ABI of libfa.so, the gfx950 (MI355X) FlashAttention forward pass,
+ * with its packed-batch, dropout and backward forms and the fused QKV
+ * projection that feeds it.  The operation below is fa_fwd's; each other
+ * entry point states how it differs.
  *
  * Operation.  For each batch b and head h, with Q, K, V the [N, d] slices at
  * (b, h) and X^ the exact value an input element stands for:
