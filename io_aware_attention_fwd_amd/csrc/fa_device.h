@@ -24,6 +24,7 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr float kLn2 = 0.69314718055994531f;
 constexpr float kRescaleThreshold = 8.0f;  // log2 of the largest probability allowed before rescaling
+constexpr float kSpeculativeSumLimit = 32768.0f;  // largest per-lane tile sum accepted without the tile's maxima
 constexpr u32 kRsrcWord3 = 0x00020000u;    // raw buffer, 32-bit data format, range-checked
 
 // ---------------------------------------------------------------- dtype traits
@@ -199,16 +200,17 @@ struct VLayout {
 // land.  Instructions [0, NPV) take two operand reads each, the rest one.
 // The sched_group_barrier sequence pins that order through scheduling (left
 // alone, the scheduler sinks each read next to its use).
-template <int I, int N, int NPV, int DEPTH>
+template <int I, int N, int NPV, int DEPTH, int MPO>
 __device__ __forceinline__ void pipeline_order() {
   if constexpr (I < N) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one matrix instruction
+    __builtin_amdgcn_sched_group_barrier(0x008, MPO, 0);  // the step's matrix instructions
     if constexpr (I + DEPTH < N) __builtin_amdgcn_sched_group_barrier(0x100, I + DEPTH < NPV ? 2 : 1, 0);  // its reads
-    pipeline_order<I + 1, N, NPV, DEPTH>();
+    pipeline_order<I + 1, N, NPV, DEPTH, MPO>();
   }
 }
 
-template <int N, int NPV, int DEPTH, class Read, class Mma>
+// MPO: matrix instructions per step (one per query block that shares the operand).
+template <int N, int NPV, int DEPTH, int MPO, class Read, class Mma>
 __device__ __forceinline__ void op_pipeline(Read read, Mma mma) {
   u32x4 buf[DEPTH];
   constexpr int P = DEPTH < N ? DEPTH : N;
@@ -221,7 +223,7 @@ __device__ __forceinline__ void op_pipeline(Read read, Mma mma) {
   }
   constexpr int kPro = (P < NPV ? P : NPV) * 2 + (P > NPV ? P - NPV : 0);
   __builtin_amdgcn_sched_group_barrier(0x100, kPro, 0);  // the first DEPTH operands' reads
-  pipeline_order<0, N, NPV, DEPTH>();
+  pipeline_order<0, N, NPV, DEPTH, MPO>();
 }
 
 }  // namespace

@@ -28,10 +28,14 @@
 //     t+1 is in flight while tile t is computed; one barrier per tile.
 //   * LDS rows are padded so that operand reads are free of bank conflicts
 //     and need no per-read address arithmetic.
-//   * Rescaling is lazy and exact: the reference maximum of a row only moves
-//     when a tile's maximum exceeds it by more than 2^8 in the exp2 domain,
-//     so probabilities stay below 256 and the accumulators are rescaled a few
-//     times per row instead of once per tile.
+//   * Rescaling is lazy and exact: the first tile sets each row's reference
+//     maximum; later tiles are exponentiated against the current reference
+//     without taking their own maxima, and only a lane whose partial sum over
+//     the tile leaves [0, 2^15] (so a probability might leave the 16-bit
+//     range of the P operand) sends its wave back to take the tile's maxima,
+//     raise the references (by more than 2^8 in the exp2 domain, or not at
+//     all), rescale O and l, and exponentiate again.  The row maxima are the
+//     one softmax step whose vector work this removes from most tiles.
 //   * Causal: tiles right of a wave's last row are skipped; tiles that cross
 //     the diagonal (and the ragged last tile) are masked element-wise.
 //   * exp is v_exp_f32 (exp2) with scale * log2(e) folded into one fma.
@@ -343,7 +347,7 @@ __global__ __launch_bounds__(NW * 64, WPE) void fa_fwd_kernel(FwdParams p) {
   // The counter is (2 * block + half, query row, slice, offset).  Dropped
   // probabilities are zeroed in the P operand only: the row sum (and so the
   // normaliser and lse) is that of the whole row.
-  auto exp_tile = [&](int kt, SArr& sc) __attribute__((always_inline)) {
+  auto exp_tile = [&](int kt, SArr& sc, float (&tsum)[S::kQB]) __attribute__((always_inline)) {
 #pragma unroll
     for (int qb = 0; qb < S::kQB; ++qb) {
       const float mb = mref[qb] == -INFINITY ? 0.f : mref[qb];
@@ -373,14 +377,40 @@ __global__ __launch_bounds__(NW * 64, WPE) void fa_fwd_kernel(FwdParams p) {
             rs[e] = sum_pair<kBf>(w, p0, p1, rs[e]);
           }
       }
-      lsum[qb] += (rs[0] + rs[1]) + (rs[2] + rs[3]);
+      tsum[qb] = (rs[0] + rs[1]) + (rs[2] + rs[3]);
     }
   };
 
+  // Tiles after the first are exponentiated against the current reference
+  // maximum without taking their own row maxima first.  The reference never
+  // exceeds the row's running maximum, so nothing underflows that the plain
+  // recurrence would keep; the danger is the other way, and a lane whose
+  // partial sum over the tile stays within kSpeculativeSumLimit has every
+  // probability within it, inside the 16-bit range of the P operand.  If any
+  // lane of the wave exceeds it (or produced inf / NaN), the wave takes the
+  // tile's maxima, raises its references, rescales, and exponentiates again.
+  // The first tile of a row always contains a visible key, so it sets a
+  // finite reference from data.  Dropout tiles always take the maxima first.
   auto softmax = [&](int kt) __attribute__((always_inline)) {
     mask_tile(kt, sacc);
+    float tsum[S::kQB];
+    if constexpr (!DROP) {
+      if (kt > 0) {
+        exp_tile(kt, sacc, tsum);
+        bool redo = false;
+#pragma unroll
+        for (int qb = 0; qb < S::kQB; ++qb) redo |= !(tsum[qb] <= kSpeculativeSumLimit);
+        if (__builtin_amdgcn_ballot_w64(redo) == 0) {
+#pragma unroll
+          for (int qb = 0; qb < S::kQB; ++qb) lsum[qb] += tsum[qb];
+          return;
+        }
+      }
+    }
     max_rescale(sacc);
-    exp_tile(kt, sacc);
+    exp_tile(kt, sacc, tsum);
+#pragma unroll
+    for (int qb = 0; qb < S::kQB; ++qb) lsum[qb] += tsum[qb];
   };
 
   // ---- V^T operands.  Element e of lane (half, col) of the V^T operand is
@@ -524,7 +554,7 @@ __global__ __launch_bounds__(NW * 64, WPE) void fa_fwd_kernel(FwdParams p) {
       if (a_pv) pv_interleaved(lv_prev);
       if (a_qk) qk_interleaved(lk);
     } else if (a_pv && a_qk) {
-      op_pipeline<kNPV + kNQK, kNPV, kDepth>(
+      op_pipeline<kNPV + kNQK, kNPV, kDepth, S::kQB>(
           [&](int i) __attribute__((always_inline)) { return i < kNPV ? pv_rd(lv_prev, i) : qk_rd(lk, i - kNPV); },
           [&](int i, u32x4 a) __attribute__((always_inline)) {
             if (i < kNPV)
@@ -533,10 +563,10 @@ __global__ __launch_bounds__(NW * 64, WPE) void fa_fwd_kernel(FwdParams p) {
               qk_op(i - kNPV, a);
           });
     } else if (a_pv) {
-      op_pipeline<kNPV, kNPV, kDepth>([&](int i) __attribute__((always_inline)) { return pv_rd(lv_prev, i); },
+      op_pipeline<kNPV, kNPV, kDepth, S::kQB>([&](int i) __attribute__((always_inline)) { return pv_rd(lv_prev, i); },
                                       [&](int i, u32x4 a) __attribute__((always_inline)) { pv_op(i, a); });
     } else if (a_qk) {
-      op_pipeline<kNQK, 0, kDepth>([&](int i) __attribute__((always_inline)) { return qk_rd(lk, i); },
+      op_pipeline<kNQK, 0, kDepth, S::kQB>([&](int i) __attribute__((always_inline)) { return qk_rd(lk, i); },
                                    [&](int i, u32x4 a) __attribute__((always_inline)) { qk_op(i, a); });
     }
     __builtin_amdgcn_s_setprio(0);
@@ -650,20 +680,25 @@ hipError_t launch_one(const FwdParams& p, hipStream_t stream) {
 // value falls back to the default).  Dropout kernels exist for the default
 // shapes only, so FA_TILE is ignored with dropout.
 constexpr Variant kVariants[] = {{32, 8, 64, 1, 2}, {32, 4, 64, 0, 4}, {32, 4, 64, 0, 3}, {32, 4, 64, 0, 2},
-                                 {64, 4, 64, 0, 2}};
+                                 {64, 4, 64, 0, 2}, {64, 8, 64, 1, 2}};
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
 // Measured on MI355X (tile sweep under rocprofv3, A/B runs in one process):
-// the ping-pong schedule wins at d = 128 for 16-bit types (fp8, with half
-// the operand bytes, prefers the plain schedule at two waves per SIMD); at
-// d = 64 the plain schedule, with 64 rows per wave for non-causal sequences
-// of 1024 rows or more and otherwise 32 rows per wave at four waves per SIMD
-// (three for fp8, and with dropout, whose generator does not fit the
-// four-wave register budget).
+// at d = 128 the ping-pong schedule wins for 16-bit types (fp8, with half the
+// operand bytes, prefers the plain schedule at two waves per SIMD).  At
+// d = 64 the softmax's vector work per tile is as long as the tile's matrix
+// work, and a single wave issues vector instructions at well under the
+// SIMD's rate, so the shapes that keep more waves in their softmax at once
+// win: 32 rows per wave at four waves per SIMD for causal masks and for
+// sequences below 4096 rows, and 64-row ping-pong waves (twice the matrix
+// work per LDS operand) for longer ones.  fp8 at d = 64 keeps the plain
+// schedule (64 rows per wave from 4096 rows on, else 32 rows at three waves
+// per SIMD).  Dropout kernels exist for the shapes listed in dispatch_dropout.
 int default_variant(Dtype dt, int d, bool causal, int N, bool dropout) {
   if (d == 128) return dt == Dtype::FP8 ? 3 : 0;  // plain at two waves per SIMD for fp8, else ping-pong
-  if (!causal && N >= 1024) return 4;     // 64 rows per wave: half the LDS operand traffic per FLOP
-  return dt == Dtype::FP8 || dropout ? 2 : 1;  // plain, three or four waves per SIMD
+  if (dropout) return !causal && N >= 1024 ? 4 : 2;
+  if (dt == Dtype::FP8) return !causal && N >= 4096 ? 4 : 2;
+  return !causal && N >= 4096 ? 5 : 1;
 }
 
 int selected_variant(Dtype dt, int d, bool causal, int N, bool dropout) {
@@ -673,7 +708,7 @@ int selected_variant(Dtype dt, int d, bool causal, int N, bool dropout) {
     if (sscanf(env, "%dx%dx%dx%dx%d", &v.qw, &v.nw, &v.bc, &v.sched, &v.wpe) == 5)
       for (int i = 0; i < kNumVariants; ++i)
         if (kVariants[i].qw == v.qw && kVariants[i].nw == v.nw && kVariants[i].bc == v.bc &&
-            kVariants[i].sched == v.sched && kVariants[i].wpe == v.wpe)
+            kVariants[i].sched == v.sched && kVariants[i].wpe == v.wpe && (i != 5 || d == 64))
           return i;
   }
   return default_variant(dt, d, causal, N, dropout);
@@ -686,6 +721,11 @@ hipError_t dispatch_variant(int v, const FwdParams& p, hipStream_t stream) {
     case 2: return launch_one<Tr, D, CAUSAL, 32, 4, 64, 0, 3, false>(p, stream);
     case 3: return launch_one<Tr, D, CAUSAL, 32, 4, 64, 0, 2, false>(p, stream);
     case 4: return launch_one<Tr, D, CAUSAL, 64, 4, 64, 0, 2, false>(p, stream);
+    case 5:
+      // 64-row ping-pong waves exist for d = 64 only (at d = 128 they would
+      // spill); selected_variant never picks them for d = 128
+      if constexpr (D == 64) return launch_one<Tr, D, CAUSAL, 64, 8, 64, 1, 2, false>(p, stream);
+      return hipErrorInvalidValue;
     default: return launch_one<Tr, D, CAUSAL, 32, 8, 64, 1, 2, false>(p, stream);
   }
 }

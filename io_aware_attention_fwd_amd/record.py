@@ -1,0 +1,182 @@
+"""Record the rocprofv3 evidence behind bench.py's roofline figures.
+
+    python -m io_aware_attention_fwd_amd.record --out-dir DIR [--shape B,H,N,d,dtype,causal]
+
+Runs ``bench.py`` under ``rocprofv3`` (each run a child process started from
+/tmp with a time limit) and writes short text summaries into DIR:
+
+* ``<tag>_kernel_stats.md``: ``--kernel-trace --stats`` of the timed bench
+  command (20 steps after 5 warm-ups), the forward kernel's average duration
+  and the TFLOP/s it implies;
+* for the headline workload only (no ``--shape``): ``<tag>_counters.md`` and
+  ``<tag>_traffic.json`` from three counter runs, ``--pmc FETCH_SIZE`` and
+  ``--pmc WRITE_SIZE`` (one counter per run, each next to a 256 MiB device
+  copy whose known size calibrates the counter) and one run of SQ counters.
+  The JSON carries the hash of the kernel sources it was taken on; bench.py
+  reports the traffic only while that hash matches the sources.
+
+``tag`` names the kernel and workload, e.g. ``fa_fwd_f16_b8h32n1024d64``.
+It needs a GPU and rocprofv3.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import json
+import os
+import subprocess
+import sys
+import tempfile
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402  (host-side helpers: FLOP and byte counts, kernel source hash)
+
+COPY_MIB = 256
+HEADLINE = (8, 32, 1024, 64, "f16", False)
+SQ_COUNTERS = ["SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CU_CYCLES",
+               "SQ_ACTIVE_INST_VALU", "SQ_WAVE_CYCLES", "SQ_WAIT_INST_LDS", "GRBM_GUI_ACTIVE"]
+
+
+def _bench_args(shape, steps, warmup, extra=()):
+    args = ["--no-sweep", "--no-cpu", "--steps", str(steps), "--warmup", str(warmup)] + list(extra)
+    if shape != HEADLINE:
+        B, H, N, d, dt, causal = shape
+        args += ["--shape", f"{B},{H},{N},{d},{dt},{int(causal)}"]
+    return args
+
+
+def _profile(prof_args, bench_args, out_dir, tag, timeout=300):
+    cmd = (["rocprofv3"] + prof_args + ["--output-format", "csv", "-d", out_dir, "-o", tag, "--",
+                                        sys.executable, os.path.join(ROOT, "bench.py")] + bench_args)
+    proc = subprocess.run(cmd, cwd="/tmp", env=dict(os.environ, TMPDIR="/tmp"), timeout=timeout,
+                          stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    # rocprofv3 may end with SIGSEGV after a complete run; the CSVs decide
+    if proc.returncode not in (0, -11, 139):
+        raise RuntimeError(f"{' '.join(cmd)} failed ({proc.returncode}):\n{proc.stdout[-2000:]}")
+    lines = [l for l in proc.stdout.splitlines() if l.startswith("{")]
+    return " ".join(prof_args), (json.loads(lines[-1]) if lines else None)
+
+
+def _counter_means(out_dir):
+    """{(is_attention_kernel, is_copy_kernel, counter): mean value per dispatch}."""
+    vals = {}
+    for f in glob.glob(os.path.join(out_dir, "**", "*_counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            key = ("fa_fwd_kernel" in r["Kernel_Name"], "copyBuffer" in r["Kernel_Name"], r["Counter_Name"])
+            vals.setdefault(key, []).append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in vals.items()}
+
+
+def _display(cmd_args, bench_args):
+    return ("cd /tmp && rocprofv3 " + cmd_args + " --output-format csv -d <out> -o <tag> -- python3 <repo>/bench.py "
+            + " ".join(bench_args))
+
+
+def tag_of(shape):
+    B, H, N, d, dt, causal = shape
+    return f"fa_fwd_{dt}_b{B}h{H}n{N}d{d}" + ("_causal" if causal else "")
+
+
+def record(shape, out_dir):
+    os.makedirs(out_dir, exist_ok=True)
+    B, H, N, d, dt, causal = shape
+    tag = tag_of(shape)
+    flop = bench.flops(B, H, N, d, causal)
+    e_in, e_out = (1, 2) if dt == "fp8" else (2, 2)
+    algo = bench.algorithmic_bytes(B, H, N, d, e_in, e_out)
+    desc = f"B={B} H={H} N={N} d={d} {dt} " + ("causal" if causal else "non-causal")
+
+    with tempfile.TemporaryDirectory(dir="/tmp") as wd:
+        bargs = _bench_args(shape, 20, 5)
+        pargs, line = _profile(["--kernel-trace", "--stats"], bargs, os.path.join(wd, "trace"), "trace")
+        stats = glob.glob(os.path.join(wd, "trace", "**", "*_kernel_stats.csv"), recursive=True)[0]
+        text = open(stats).read().strip()
+        row = [r for r in csv.DictReader(open(stats)) if "fa_fwd_kernel" in r["Name"]][0]
+        avg_ns = float(row["AverageNs"])
+        with open(os.path.join(out_dir, f"{tag}_kernel_stats.md"), "w") as f:
+            f.write(f"# rocprofv3 kernel statistics: attention forward {desc}\n\n")
+            f.write(f"Command (MI355X, repository root as `<repo>`):\n\n```\n{_display(pargs, bargs)}\n```\n\n")
+            f.write(f"`kernel_stats.csv` as written by rocprofv3:\n\n```\n{text}\n```\n\n")
+            f.write(f"Average duration of the attention kernel {avg_ns / 1e3:.1f} us -> "
+                    f"{flop / avg_ns / 1e3:.1f} TFLOP/s ({flop / 1e9:.1f} GFLOP per launch).")
+            if line:
+                f.write(f"  The same command's bench.py line (HIP events over the timed region, profiler attached) "
+                        f"reported {line['ms_per_step'] * 1e3:.1f} us per step, {line['value']:.1f} TFLOP/s.")
+            f.write(f"\n\nKernel source hash (bench.kernel_source_hash): {bench.kernel_source_hash()}\n")
+        if shape != HEADLINE:
+            return
+
+        raw, factor, cmds = {}, {}, []
+        for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+            bargs = _bench_args(shape, 3, 1, ["--copy-calib-mib", str(COPY_MIB)])
+            pargs, _ = _profile(["--pmc", counter], bargs, os.path.join(wd, counter), counter.lower())
+            cmds.append(_display(pargs, bargs))
+            c = _counter_means(os.path.join(wd, counter))
+            raw[counter] = c[(True, False, counter)]
+            raw[counter + "_copy"] = c[(False, True, counter)]
+            factor[counter] = COPY_MIB * 1024 / raw[counter + "_copy"]
+        bargs = _bench_args(shape, 3, 1)
+        pargs, _ = _profile(["--pmc"] + SQ_COUNTERS, bargs, os.path.join(wd, "sq"), "sq")
+        sq_cmd = _display(pargs, bargs)
+        sq = {k[2]: v for k, v in _counter_means(os.path.join(wd, "sq")).items() if k[0]}
+
+    fetch = round(raw["FETCH_SIZE"] * 1024 * factor["FETCH_SIZE"])
+    write = round(raw["WRITE_SIZE"] * 1024 * factor["WRITE_SIZE"])
+    traffic = {
+        "kernel": row["Name"], "workload": f"attention forward {desc}",
+        "kernel_source_sha256_16": bench.kernel_source_hash(),
+        "fetch_size_kib_per_dispatch_raw": raw["FETCH_SIZE"], "write_size_kib_per_dispatch_raw": raw["WRITE_SIZE"],
+        "calibration": {"reference_kernel": f"__amd_rocclr_copyBuffer (device copy of {COPY_MIB} MiB)",
+                        "expected_kib_each_way": COPY_MIB * 1024,
+                        "fetch_size_kib_raw": raw["FETCH_SIZE_copy"], "write_size_kib_raw": raw["WRITE_SIZE_copy"],
+                        "fetch_factor": round(factor["FETCH_SIZE"], 5), "write_factor": round(factor["WRITE_SIZE"], 5)},
+        "fetch_bytes_per_launch": fetch, "write_bytes_per_launch": write, "bytes_per_launch": fetch + write,
+        "algorithmic_bytes_per_launch": algo, "ratio_to_algorithmic": round((fetch + write) / algo, 4),
+        "commands": cmds,
+    }
+    with open(os.path.join(out_dir, f"{tag}_traffic.json"), "w") as f:
+        json.dump(traffic, f, indent=1)
+        f.write("\n")
+    grbm = sq.get("GRBM_GUI_ACTIVE", float("nan"))
+    mfma = sq.get("SQ_VALU_MFMA_BUSY_CYCLES", float("nan"))
+    with open(os.path.join(out_dir, f"{tag}_counters.md"), "w") as f:
+        f.write(f"# rocprofv3 counters: attention forward {desc}\n\nKernel: `{row['Name']}`\n\n")
+        f.write("## HBM traffic (FETCH_SIZE, WRITE_SIZE; one counter per run)\n\n")
+        for c in cmds:
+            f.write(f"```\n{c}\n```\n\n")
+        f.write(f"Calibration: the same run performs one {COPY_MIB} MiB device copy (`__amd_rocclr_copyBuffer`), "
+                f"which must read and write {COPY_MIB * 1024} KiB.  It reads FETCH_SIZE = {raw['FETCH_SIZE_copy']:.1f} "
+                f"KiB and WRITE_SIZE = {raw['WRITE_SIZE_copy']:.1f} KiB, so FETCH_SIZE is scaled by "
+                f"{factor['FETCH_SIZE']:.4f} and WRITE_SIZE by {factor['WRITE_SIZE']:.4f}.\n\n")
+        f.write("| | raw KiB per dispatch | scaled bytes per launch |\n|---|---|---|\n")
+        f.write(f"| FETCH_SIZE | {raw['FETCH_SIZE']:.1f} | {fetch} |\n| WRITE_SIZE | {raw['WRITE_SIZE']:.1f} | {write} |\n")
+        f.write(f"| total | | {fetch + write} |\n\n")
+        f.write(f"Algorithmic bytes per launch (Q, K, V read once, O and lse written once): {algo}.  "
+                f"Measured / algorithmic = {(fetch + write) / algo:.4f}.\n\n")
+        f.write(f"## SQ counters (one run)\n\n```\n{sq_cmd}\n```\n\n| counter | mean per dispatch |\n|---|---|\n")
+        for k in sorted(sq):
+            f.write(f"| {k} | {sq[k]:.0f} |\n")
+        f.write(f"\nGRBM_GUI_ACTIVE is summed over the 8 XCDs ({grbm / 8:.0f} cycles each); MFMA busy / "
+                f"(cycles x 1024 SIMDs) = {100 * mfma / (grbm / 8 * 1024):.1f}% under the counter run.\n")
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--out-dir", required=True)
+    ap.add_argument("--shape", default=None, help="B,H,N,d,dtype,causal (default: the headline workload)")
+    args = ap.parse_args(argv)
+    shape = HEADLINE
+    if args.shape:
+        B, H, N, d, dt, causal = args.shape.split(",")
+        shape = (int(B), int(H), int(N), int(d), dt, causal in ("1", "true"))
+    record(shape, args.out_dir)
+    print(f"recorded {tag_of(shape)} into {args.out_dir}", flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

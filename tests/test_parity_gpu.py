@@ -178,3 +178,38 @@ def test_long_sequences_sampled_rows(N, d, dtype, causal):
             o_ref, lse_ref = oracle.attention_slice(q[i:i + 1], k[:n_vis], v[:n_vis], scale, False)
             assert np.abs(o_np[0, h, i] - o_ref[0]).max() <= gu.O_TOL[dtype], (h, i)
             assert abs(lse_np[0, h, i] - lse_ref[0]) <= gu.LSE_TOL * max(1.0, abs(lse_ref[0])), (h, i)
+
+
+def _growing_scores(B, H, N, d, dtype, jumps, seed=5):
+    """Q and K aligned with one shared direction so that every query's scores
+    step up (in the exp2 domain, scale*log2(e)*q.k) by jumps[t] at key tile
+    t (64 keys); V i.i.d. N(0,1).  The first tile sets the row references and
+    the later ones exceed them by the accumulated jumps."""
+    rng = np.random.default_rng(seed)
+    u = rng.standard_normal(d).astype(np.float32)
+    u /= np.linalg.norm(u)
+    scale = 1 / math.sqrt(d)
+    level = np.cumsum([0.0] + list(jumps))  # exp2-domain offset of each tile
+    t = level[np.minimum(np.arange(N) // 64, len(level) - 1)] / (scale * math.log2(math.e) * 4.0)
+    q = (4.0 * u + 0.3 * rng.standard_normal((B, H, N, d))).astype(np.float32)
+    k = (t[:, None] * u + 0.3 * rng.standard_normal((B, H, N, d))).astype(np.float32)
+    v = rng.standard_normal((B, H, N, d)).astype(np.float32)
+    return gen.store(dtype, q, k, v), scale
+
+
+# jumps per key tile, in the exp2 domain (tile maxima sit ~3 above them with
+# the noise): 7 keeps every later tile's partial sums below 2^15, so the tiles
+# are accepted against the first tile's references with probabilities up to
+# ~2^10 (the old rule rescaled above 2^8); 30 leaves the 16-bit range (the
+# tile's maxima are taken and the rows rescaled); the ramp and the mix do both
+# along the sequence.
+@pytest.mark.parametrize("jumps", [[7.0], [30.0], [12.0] * 9, [3.0, 7.0, 25.0, 0.0, 40.0]],
+                         ids=["step7", "step30", "ramp12", "mixed"])
+@pytest.mark.parametrize("dtype,d", [("f16", 64), ("bf16", 64), ("fp8", 64), ("f16", 128), ("bf16", 128)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_growing_scores_rescale(jumps, dtype, d, causal):
+    B, H, N = 1, 2, 640
+    print(f"[growing] jumps={jumps} {dtype} d={d} causal={causal}", flush=True)
+    x, scale = _growing_scores(B, H, N, d, dtype, jumps)
+    o, lse = gu.run_gpu(x, scale, causal)
+    gu.compare(x, gu.o_to_numpy(o), lse.cpu().numpy().astype(np.float64), scale, causal)
