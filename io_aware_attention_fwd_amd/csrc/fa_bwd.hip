@@ -143,8 +143,9 @@ __device__ __forceinline__ void store_rowT(char* row_ptr, const f32x16 (&acc)[D 
 }  // namespace
 
 // ---------------------------------------------------------------- dQ kernel
-template <class Tr, int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(BwdParams p) {
+// WPE: minimum waves per SIMD the registers are budgeted for.
+template <class Tr, int D, bool CAUSAL, int WPE>
+__global__ __launch_bounds__(256, WPE) void fa_bwd_dq_kernel(BwdParams p) {
   constexpr int NW = 4, BC = 64, kKB = 2;
   constexpr bool kBf = Tr::kPvBf16;
   using B = BwdShape<D>;
@@ -410,7 +411,7 @@ namespace {
 
 template <class Tr, int D, bool CAUSAL>
 hipError_t launch_bwd_typed(const BwdParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL((fa_bwd_dq_kernel<Tr, D, CAUSAL>), dim3(p.total_wg), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((fa_bwd_dq_kernel<Tr, D, CAUSAL, D == 64 ? 3 : 2>), dim3(p.total_wg), dim3(256), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // (256 CUs: at d = 128 two waves per SIMD pay off once there are two

@@ -94,7 +94,7 @@ struct Shape {
 template <class Tr, int D, bool CAUSAL, int QW, int NW, int BC, int SCHED, int WPE, bool DROP>
 __global__ __launch_bounds__(NW * 64, WPE) void fa_fwd_kernel(FwdParams p) {
   constexpr bool PP = SCHED == 1;
-  static_assert(!PP || NW == 8, "the ping-pong schedule pairs waves w and w+4 on one SIMD");
+  static_assert(!PP || NW == 8 || NW == 16, "the ping-pong schedule splits the waves into two groups that each hold NW/8 waves of every SIMD");
   using S = Shape<Tr, D, QW, NW, BC>;
   constexpr bool kBf = Tr::kPvBf16;
   // Two LDS stages.  Separate arrays let the compiler tell the
@@ -512,18 +512,21 @@ __global__ __launch_bounds__(NW * 64, WPE) void fa_fwd_kernel(FwdParams p) {
     return kt >= 0 && kt < n_kv && qw0 < N && !(CAUSAL && kt * BC > qw0 + QW - 1);
   };
 
-  // ---- main loop: ping-pong between the two waves of each SIMD.
-  // Waves 0-3 (group 0) and 4-7 (group 1) share the four SIMDs pairwise.
+  // ---- main loop: ping-pong between two groups of waves on each SIMD.
+  // Waves are dealt to the four SIMDs round-robin, so the first and second
+  // halves of the workgroup (group 0 and group 1) each hold NW/8 waves of
+  // every SIMD: one each with 8 waves, two each with 16 (whose softmax then
+  // runs on two waves of a SIMD at once, at the higher two-wave issue rate).
   // Time is cut into phases separated by workgroup barriers; in every phase
   // one group runs matrix-core work (P V of the previous tile, Q K^T of the
   // current one) while the other runs the softmax of the tile it has scores
-  // for, so each SIMD overlaps one wave's MFMAs with the other's VALU work.
+  // for, so each SIMD overlaps MFMAs of one group with VALU work of the other.
   //   phase 2t   : group 0 MFMA(t)            group 1 softmax(t-1)
   //   phase 2t+1 : group 0 softmax(t)         group 1 MFMA(t)
   // K(t) lives in stage t%2 for phases 2t..2t+1; V(t) in stage t%2 for phases
   // 2t+2..2t+3.  Both are issued at phase 2t (K one tile ahead) and waited for
   // at the end of phase 2t+1.
-  const int group = wave >> 2;
+  const int group = wave / (NW / 2);
   // Matrix phase: P V of the previous tile, then Q K^T of this one.  For
   // 16-bit types both run as one pipelined stream of instructions (P V in
   // (kb, t, db) order, db fastest, so consecutive instructions feed
@@ -532,7 +535,7 @@ __global__ __launch_bounds__(NW * 64, WPE) void fa_fwd_kernel(FwdParams p) {
   // vector-heavy softmax, and the matrix stream should not wait behind it.
   constexpr int kNPV = S::kDB * S::kKB * 2;
   constexpr int kNQK = S::kKB * S::kQSteps;
-  constexpr int kDepth = 4;
+  constexpr int kDepth = WPE >= 4 ? 2 : 4;  // operand reads in flight (fewer at four waves per SIMD: 128 registers)
   auto pv_op = [&](int i, u32x4 a) __attribute__((always_inline)) {
     const int db = i % S::kDB, t = (i / S::kDB) % 2, kb = i / (2 * S::kDB);
 #pragma unroll
@@ -680,25 +683,32 @@ hipError_t launch_one(const FwdParams& p, hipStream_t stream) {
 // value falls back to the default).  Dropout kernels exist for the default
 // shapes only, so FA_TILE is ignored with dropout.
 constexpr Variant kVariants[] = {{32, 8, 64, 1, 2}, {32, 4, 64, 0, 4}, {32, 4, 64, 0, 3}, {32, 4, 64, 0, 2},
-                                 {64, 4, 64, 0, 2}, {64, 8, 64, 1, 2}};
+                                 {64, 4, 64, 0, 2}, {64, 8, 64, 1, 2}, {32, 16, 64, 1, 4}};
+// Shapes compiled for d = 64 only (at d = 128 they would spill).
+constexpr bool d64_only(int v) { return v == 5 || v == 6; }
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
-// Measured on MI355X (tile sweep under rocprofv3, A/B runs in one process):
-// at d = 128 the ping-pong schedule wins for 16-bit types (fp8, with half the
-// operand bytes, prefers the plain schedule at two waves per SIMD).  At
-// d = 64 the softmax's vector work per tile is as long as the tile's matrix
-// work, and a single wave issues vector instructions at well under the
-// SIMD's rate, so the shapes that keep more waves in their softmax at once
-// win: 32 rows per wave at four waves per SIMD for causal masks and for
-// sequences below 4096 rows, and 64-row ping-pong waves (twice the matrix
-// work per LDS operand) for longer ones.  fp8 at d = 64 keeps the plain
-// schedule (64 rows per wave from 4096 rows on, else 32 rows at three waves
-// per SIMD).  Dropout kernels exist for the shapes listed in dispatch_dropout.
+// Measured on MI355X (tile sweep under rocprofv3, interleaved A/B runs in one
+// process): at d = 128 the ping-pong schedule wins for 16-bit types (fp8,
+// with half the operand bytes, prefers the plain schedule at two waves per
+// SIMD).  At d = 64 the softmax's vector work per tile is as long as the
+// tile's matrix work, and a single wave issues vector instructions at well
+// under the SIMD's rate, so the shapes that keep more waves in their softmax
+// at once win: 32 rows per wave at four waves per SIMD for causal masks and
+// short sequences; for longer ones the ping-pong schedule, with 16 waves of
+// 32 rows (two waves of each SIMD in each phase) for binary16 from 2048
+// rows, and 8 waves of 64 rows (twice the matrix work per LDS operand) for
+// bfloat16 from 4096 rows, whose row sums take twice the vector work.  fp8
+// at d = 64 keeps the plain schedule (64 rows per wave from 4096 rows on,
+// else 32 rows at three waves per SIMD).  Dropout kernels exist for the
+// shapes listed in dispatch_dropout.
 int default_variant(Dtype dt, int d, bool causal, int N, bool dropout) {
   if (d == 128) return dt == Dtype::FP8 ? 3 : 0;  // plain at two waves per SIMD for fp8, else ping-pong
   if (dropout) return !causal && N >= 1024 ? 4 : 2;
   if (dt == Dtype::FP8) return !causal && N >= 4096 ? 4 : 2;
-  return !causal && N >= 4096 ? 5 : 1;
+  if (causal) return 1;
+  if (dt == Dtype::F16) return N >= 2048 ? 6 : 1;
+  return N >= 4096 ? 5 : 1;
 }
 
 int selected_variant(Dtype dt, int d, bool causal, int N, bool dropout) {
@@ -708,7 +718,7 @@ int selected_variant(Dtype dt, int d, bool causal, int N, bool dropout) {
     if (sscanf(env, "%dx%dx%dx%dx%d", &v.qw, &v.nw, &v.bc, &v.sched, &v.wpe) == 5)
       for (int i = 0; i < kNumVariants; ++i)
         if (kVariants[i].qw == v.qw && kVariants[i].nw == v.nw && kVariants[i].bc == v.bc &&
-            kVariants[i].sched == v.sched && kVariants[i].wpe == v.wpe && (i != 5 || d == 64))
+            kVariants[i].sched == v.sched && kVariants[i].wpe == v.wpe && (!d64_only(i) || d == 64))
           return i;
   }
   return default_variant(dt, d, causal, N, dropout);
@@ -725,6 +735,9 @@ hipError_t dispatch_variant(int v, const FwdParams& p, hipStream_t stream) {
       // 64-row ping-pong waves exist for d = 64 only (at d = 128 they would
       // spill); selected_variant never picks them for d = 128
       if constexpr (D == 64) return launch_one<Tr, D, CAUSAL, 64, 8, 64, 1, 2, false>(p, stream);
+      return hipErrorInvalidValue;
+    case 6:
+      if constexpr (D == 64) return launch_one<Tr, D, CAUSAL, 32, 16, 64, 1, 4, false>(p, stream);
       return hipErrorInvalidValue;
     default: return launch_one<Tr, D, CAUSAL, 32, 8, 64, 1, 2, false>(p, stream);
   }
