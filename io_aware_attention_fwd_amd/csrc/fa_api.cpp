@@ -49,7 +49,7 @@ int forward(const void* q, const void* k, const void* v, void* o, float* lse, co
   if (!isfinite(scale) || !isfinite(q_descale) || !isfinite(k_descale) || !isfinite(v_descale)) return FA_ERR_SCALE;
   const int eb = elem_bytes(dt);
   const int ob = 2;  // O is binary16 / bfloat16 (bfloat16 for fp8 inputs)
-  const int br = fa::rows_per_workgroup(dt, d, causal != 0, L.N, drop.t < 256);
+  const int br = fa::rows_per_workgroup(dt, d, causal != 0, L.N, drop.t < 256, packed);
   // The rows of one (sequence, head), plus the padding rows of its last tile,
   // must be addressable with 32-bit byte offsets (the kernels use buffer loads).
   const int64_t in_row = packed ? (int64_t)L.H * d * eb : (int64_t)d * eb;

@@ -81,8 +81,9 @@ ProjTiling proj_tiling(int64_t M, int64_t ncol);
 
 enum class Dtype { F16 = 0, BF16 = 1, FP8 = 2 };
 
-// Rows of Q one workgroup owns for the instance chosen for this call (sizes the grid).
-int rows_per_workgroup(Dtype dt, int d, bool causal, int N, bool dropout);
+// Rows of Q one workgroup owns for the instance chosen for this call (sizes the
+// grid).  packed: sequences of different lengths (cu_seqlens), N their maximum.
+int rows_per_workgroup(Dtype dt, int d, bool causal, int N, bool dropout, bool packed);
 
 // Enqueue one forward pass; returns hipSuccess or the launch error.
 hipError_t launch_fwd(Dtype dt, int d, bool causal, const FwdParams& p, hipStream_t stream);

@@ -16,6 +16,13 @@ Runs ``bench.py`` under ``rocprofv3`` (each run a child process started from
   reports the traffic only while that hash matches the sources.
 
 ``tag`` names the kernel and workload, e.g. ``fa_fwd_f16_b8h32n1024d64``.
+
+    python -m io_aware_attention_fwd_amd.record --out-dir DIR --mode MODE --mode-arg ARG --tag TAG
+
+profiles another bench.py mode (``varlen``, ``dropout``, ``bwd``, ``proj``;
+``--MODE ARG`` on bench.py's command line) the same way: ``TAG_kernel_stats.md``
+with every kernel of the run, and the FLOP per step that bench.py reports
+divided by the summed average durations of the kernels one step launches.
 It needs a GPU and rocprofv3.
 """
 from __future__ import annotations
@@ -164,11 +171,46 @@ def record(shape, out_dir):
                 f"(cycles x 1024 SIMDs) = {100 * mfma / (grbm / 8 * 1024):.1f}% under the counter run.\n")
 
 
+def record_mode(mode, mode_arg, tag, out_dir):
+    """Kernel statistics of bench.py --MODE ARG (one step may launch several kernels)."""
+    os.makedirs(out_dir, exist_ok=True)
+    bargs = ["--no-sweep", "--no-cpu", f"--{mode}", mode_arg, "--steps", "10", "--warmup", "3"]
+    with tempfile.TemporaryDirectory(dir="/tmp") as wd:
+        pargs, line = _profile(["--kernel-trace", "--stats"], bargs, os.path.join(wd, "trace"), "trace")
+        stats = glob.glob(os.path.join(wd, "trace", "**", "*_kernel_stats.csv"), recursive=True)[0]
+        text = open(stats).read().strip()
+        rows = [r for r in csv.DictReader(open(stats)) if r["Name"].startswith("void fa::")]
+    # the kernels launched once per step are the most-called ones (a kernel
+    # called once, like the forward pass that feeds the backward, is set-up)
+    most = max(int(r["Calls"]) for r in rows)
+    per_step_ns = sum(float(r["AverageNs"]) for r in rows if int(r["Calls"]) == most)
+    with open(os.path.join(out_dir, f"{tag}_kernel_stats.md"), "w") as f:
+        f.write(f"# rocprofv3 kernel statistics: bench.py --{mode} {mode_arg}\n\n")
+        f.write(f"Command (MI355X, repository root as `<repo>`):\n\n```\n{_display(pargs, bargs)}\n```\n\n")
+        f.write(f"`kernel_stats.csv` as written by rocprofv3:\n\n```\n{text}\n```\n\n")
+        for r in rows:
+            f.write(f"* `{r['Name']}`: {int(r['Calls'])} calls, average {float(r['AverageNs']) / 1e3:.1f} us\n")
+        if line:
+            flop = line["value"] * 1e12 * line["ms_per_step"] * 1e-3
+            f.write(f"\nThe kernels of one step take {per_step_ns / 1e3:.1f} us on average -> "
+                    f"{flop / per_step_ns / 1e3:.1f} TFLOP/s at bench.py's {flop / 1e9:.1f} GFLOP per step.  The same "
+                    f"command's bench.py line (HIP events over the timed region, profiler attached) reported "
+                    f"{line['ms_per_step'] * 1e3:.1f} us per step, {line['value']:.1f} TFLOP/s.\n")
+        f.write(f"\nKernel source hash (bench.kernel_source_hash): {bench.kernel_source_hash()}\n")
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--out-dir", required=True)
     ap.add_argument("--shape", default=None, help="B,H,N,d,dtype,causal (default: the headline workload)")
+    ap.add_argument("--mode", default=None, choices=["varlen", "dropout", "bwd", "proj"])
+    ap.add_argument("--mode-arg", default=None, help="the argument bench.py takes for --MODE")
+    ap.add_argument("--tag", default=None, help="file name stem for --mode")
     args = ap.parse_args(argv)
+    if args.mode:
+        record_mode(args.mode, args.mode_arg, args.tag, args.out_dir)
+        print(f"recorded {args.tag} into {args.out_dir}", flush=True)
+        return 0
     shape = HEADLINE
     if args.shape:
         B, H, N, d, dt, causal = args.shape.split(",")
