@@ -683,9 +683,9 @@ hipError_t launch_one(const FwdParams& p, hipStream_t stream) {
 // value falls back to the default).  Dropout kernels exist for the default
 // shapes only, so FA_TILE is ignored with dropout.
 constexpr Variant kVariants[] = {{32, 8, 64, 1, 2}, {32, 4, 64, 0, 4}, {32, 4, 64, 0, 3}, {32, 4, 64, 0, 2},
-                                 {64, 4, 64, 0, 2}, {64, 8, 64, 1, 2}, {32, 16, 64, 1, 4}};
+                                 {64, 4, 64, 0, 2}, {64, 8, 64, 1, 2}, {32, 16, 64, 1, 4}, {32, 8, 64, 0, 4}};
 // Shapes compiled for d = 64 only (at d = 128 they would spill).
-constexpr bool d64_only(int v) { return v == 5 || v == 6; }
+constexpr bool d64_only(int v) { return v == 5 || v == 6 || v == 7; }
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
 // Measured on MI355X (tile sweep under rocprofv3, interleaved A/B runs in one
@@ -694,25 +694,26 @@ constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 // SIMD).  At d = 64 the softmax's vector work per tile is as long as the
 // tile's matrix work, and a single wave issues vector instructions at well
 // under the SIMD's rate, so the shapes that keep more waves in their softmax
-// at once win: 32 rows per wave at four waves per SIMD for causal masks and
-// short sequences; for longer ones the ping-pong schedule, with 16 waves of
-// 32 rows (two waves of each SIMD in each phase) for binary16 from 2048
-// rows, and 8 waves of 64 rows (twice the matrix work per LDS operand) for
-// bfloat16 from 4096 rows, whose row sums take twice the vector work.  fp8
-// at d = 64 keeps the plain schedule (64 rows per wave from 4096 rows on,
-// else 32 rows at three waves per SIMD).  Packed batches of mixed lengths
-// (N = the longest) keep 128-row workgroups for 16-bit types: the larger
-// ping-pong workgroups idle most of their waves on the short sequences
-// (lengths 256..4096: 660 against 596 TFLOP/s at d = 64, 726 against 699 at
-// d = 128).  Dropout kernels exist for the shapes listed in dispatch_dropout.
+// at once win: 32 rows per wave at four waves per SIMD.  Without a causal
+// mask, 8 such waves per workgroup (each K/V tile in LDS then serves 256
+// query rows, half the tile loads per row of 4 waves) for binary16 and fp8
+// at every length and for bfloat16 below 4096 rows; from 4096 rows on,
+// bfloat16 (whose row sums take twice the vector work) prefers 64-row
+// ping-pong waves (twice the matrix work per LDS operand) and fp8 the plain
+// 64-row shape, both by a few percent.  With the causal mask the 4-wave
+// workgroups win: a workgroup waits for its longest wave, and the causal
+// row lengths differ more across 256 rows.  Packed batches of mixed lengths
+// (N = the longest) keep 128-row workgroups for 16-bit types: larger ones
+// idle most of their waves on the short sequences (lengths 256..4096: 660
+// against 596 TFLOP/s at d = 64, 726 against 699 at d = 128).  Dropout
+// kernels exist for the shapes listed in dispatch_dropout.
 int default_variant(Dtype dt, int d, bool causal, int N, bool dropout, bool packed) {
   if (packed && !dropout && dt != Dtype::FP8) return d == 128 ? 3 : 1;
   if (d == 128) return dt == Dtype::FP8 ? 3 : 0;  // plain at two waves per SIMD for fp8, else ping-pong
   if (dropout) return !causal && N >= 1024 ? 4 : 2;
-  if (dt == Dtype::FP8) return !causal && N >= 4096 ? 4 : 2;
-  if (causal) return 1;
-  if (dt == Dtype::F16) return N >= 2048 ? 6 : 1;
-  return N >= 4096 ? 5 : 1;
+  if (causal) return dt == Dtype::FP8 ? 2 : 1;
+  if (N >= 4096 && dt != Dtype::F16) return dt == Dtype::FP8 ? 4 : 5;
+  return 7;
 }
 
 int selected_variant(Dtype dt, int d, bool causal, int N, bool dropout, bool packed) {
@@ -742,6 +743,9 @@ hipError_t dispatch_variant(int v, const FwdParams& p, hipStream_t stream) {
       return hipErrorInvalidValue;
     case 6:
       if constexpr (D == 64) return launch_one<Tr, D, CAUSAL, 32, 16, 64, 1, 4, false>(p, stream);
+      return hipErrorInvalidValue;
+    case 7:
+      if constexpr (D == 64) return launch_one<Tr, D, CAUSAL, 32, 8, 64, 0, 4, false>(p, stream);
       return hipErrorInvalidValue;
     default: return launch_one<Tr, D, CAUSAL, 32, 8, 64, 1, 2, false>(p, stream);
   }

@@ -125,7 +125,7 @@ def main(argv=None):
     results = []
     for w in args.workloads:
         for t in tiles:
-            if t in ("64x8x64x1x2", "32x16x64x1x4") and int(w.split(",")[3]) != 64:
+            if t in ("64x8x64x1x2", "32x16x64x1x4", "32x8x64x0x4") and int(w.split(",")[3]) != 64:
                 continue  # 64-row ping-pong waves are compiled for d = 64 only
             with tempfile.TemporaryDirectory(dir="/tmp") as wd:
                 r = measure(t, w, wd)
