@@ -200,19 +200,23 @@ struct VLayout {
 // land.  Instructions [0, NPV) take two operand reads each, the rest one.
 // The sched_group_barrier sequence pins that order through scheduling (left
 // alone, the scheduler sinks each read next to its use).
-template <int I, int N, int NPV, int DEPTH, int MPO>
+template <int I, int N, int NPV, int DEPTH, int MPO, int QKR>
 __device__ __forceinline__ void pipeline_order() {
   if constexpr (I < N) {
     __builtin_amdgcn_sched_group_barrier(0x008, MPO, 0);  // the step's matrix instructions
-    if constexpr (I + DEPTH < N) __builtin_amdgcn_sched_group_barrier(0x100, I + DEPTH < NPV ? 2 : 1, 0);  // its reads
-    pipeline_order<I + 1, N, NPV, DEPTH, MPO>();
+    if constexpr (I + DEPTH < N) __builtin_amdgcn_sched_group_barrier(0x100, I + DEPTH < NPV ? 2 : QKR, 0);  // its reads
+    pipeline_order<I + 1, N, NPV, DEPTH, MPO, QKR>();
   }
 }
 
-// MPO: matrix instructions per step (one per query block that shares the operand).
-template <int N, int NPV, int DEPTH, int MPO, class Read, class Mma>
+// MPO: matrix instructions per step (one per query block that shares the
+// operand).  QKR: LDS reads per step from NPV on (1, or 2 where a step also
+// reads a query operand from LDS).  Read returns the step's operands, of one
+// type for every step.
+template <int N, int NPV, int DEPTH, int MPO, int QKR = 1, class Read, class Mma>
 __device__ __forceinline__ void op_pipeline(Read read, Mma mma) {
-  u32x4 buf[DEPTH];
+  using Op = decltype(read(0));
+  Op buf[DEPTH];
   constexpr int P = DEPTH < N ? DEPTH : N;
 #pragma unroll
   for (int i = 0; i < P; ++i) buf[i] = read(i);
@@ -221,9 +225,9 @@ __device__ __forceinline__ void op_pipeline(Read read, Mma mma) {
     mma(i, buf[i % DEPTH]);
     if (i + DEPTH < N) buf[i % DEPTH] = read(i + DEPTH);
   }
-  constexpr int kPro = (P < NPV ? P : NPV) * 2 + (P > NPV ? P - NPV : 0);
+  constexpr int kPro = (P < NPV ? P : NPV) * 2 + (P > NPV ? P - NPV : 0) * QKR;
   __builtin_amdgcn_sched_group_barrier(0x100, kPro, 0);  // the first DEPTH operands' reads
-  pipeline_order<0, N, NPV, DEPTH, MPO>();
+  pipeline_order<0, N, NPV, DEPTH, MPO, QKR>();
 }
 
 }  // namespace

@@ -105,11 +105,19 @@ __global__ __launch_bounds__(NW * 64, WPE) void fa_fwd_kernel(FwdParams p) {
   __shared__ __attribute__((aligned(16))) char lds_v0[S::kAllocV];
   __shared__ __attribute__((aligned(16))) char lds_v1[S::kAllocV];
 
+  // With 64-row waves at d = 128 and 16-bit values the second 32-row query
+  // block's Q operands live in LDS (one padded row per query, laid out like a
+  // K tile), so that the O accumulators and scores fit the register budget of
+  // two waves per SIMD; each wave reads only its own rows.
+  constexpr bool kQ1Lds = !Tr::kFp8 && QW == 64 && D == 128;
+  __shared__ __attribute__((aligned(16))) char lds_q1[kQ1Lds ? NW * 32 * S::kRSK : 16];
+
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int half = lane >> 5;
   const int l32 = lane & 31;
+  const int q1base = (wave * 32 + l32) * S::kRSK + 16 * half;  // this lane's row of lds_q1, k-group `half`
 
   const int tile = xcd_remap(blockIdx.x, p.total_wg);
   const int bh = tile / p.n_qtiles;
@@ -162,10 +170,18 @@ __global__ __launch_bounds__(NW * 64, WPE) void fa_fwd_kernel(FwdParams p) {
         u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rq, row * rowb + (16 * s + 8 * half) * 2, 0, 0);
 #pragma unroll
         for (int e = 0; e < 4; ++e) x[e] = (x[e] ^ p.q_xor) & p.q_and;
-        q16[qb][s] = x;
+        if (kQ1Lds && qb == 1)
+          *reinterpret_cast<u32x4*>(lds_q1 + q1base + 32 * s) = x;
+        else
+          q16[qb][s] = x;
       }
     }
   }
+
+  // B operand of query block qb, instruction step s (16-bit values)
+  auto qop = [&](int qb, int s) __attribute__((always_inline)) {
+    return kQ1Lds && qb == 1 ? lds_read_b128(lds_q1, q1base + 32 * s) : q16[qb][s];
+  };
 
   const int n_all = (N + BC - 1) / BC;
   const int n_kv = CAUSAL ? min(n_all, (q0 + S::kBR - 1) / BC + 1) : n_all;
@@ -279,7 +295,7 @@ __global__ __launch_bounds__(NW * 64, WPE) void fa_fwd_kernel(FwdParams p) {
           if constexpr (Tr::kFp8)
             dst[kb][qb] = mfma_fp8(kop8[kb][s], q8[qb][s], dst[kb][qb]);
           else
-            dst[kb][qb] = mfma16(kop16[kb][s], q16[qb][s], dst[kb][qb], kBf);
+            dst[kb][qb] = mfma16(kop16[kb][s], qop(qb, s), dst[kb][qb], kBf);
         }
     }
   };
@@ -494,7 +510,7 @@ __global__ __launch_bounds__(NW * 64, WPE) void fa_fwd_kernel(FwdParams p) {
         } else {
           const u32x4 a = k_read16(lk, kb, s);
 #pragma unroll
-          for (int qb = 0; qb < S::kQB; ++qb) sacc[kb][qb] = mfma16(a, q16[qb][s], sacc[kb][qb], kBf);
+          for (int qb = 0; qb < S::kQB; ++qb) sacc[kb][qb] = mfma16(a, qop(qb, s), sacc[kb][qb], kBf);
         }
       }
     }
@@ -535,21 +551,33 @@ __global__ __launch_bounds__(NW * 64, WPE) void fa_fwd_kernel(FwdParams p) {
   // vector-heavy softmax, and the matrix stream should not wait behind it.
   constexpr int kNPV = S::kDB * S::kKB * 2;
   constexpr int kNQK = S::kKB * S::kQSteps;
-  constexpr int kDepth = WPE >= 4 ? 2 : 4;  // operand reads in flight (fewer at four waves per SIMD: 128 registers)
-  auto pv_op = [&](int i, u32x4 a) __attribute__((always_inline)) {
+  // operand reads in flight (fewer where registers are short: four waves per
+  // SIMD, or 64-row waves at d = 128)
+  constexpr int kDepth = WPE >= 4 || (QW == 64 && D == 128) ? 2 : 4;
+  // A step's LDS operands: the A operand, and for Q K^T steps with kQ1Lds the
+  // second query block's B operand (left unused, and so never read, otherwise).
+  struct Ops {
+    u32x4 a, q1;
+  };
+  constexpr int kQKReads = kQ1Lds ? 2 : 1;
+  auto pv_op = [&](int i, Ops o) __attribute__((always_inline)) {
     const int db = i % S::kDB, t = (i / S::kDB) % 2, kb = i / (2 * S::kDB);
 #pragma unroll
-    for (int qb = 0; qb < S::kQB; ++qb) oacc[db][qb] = mfma16(a, pb[kb][qb][t], oacc[db][qb], kBf);
+    for (int qb = 0; qb < S::kQB; ++qb) oacc[db][qb] = mfma16(o.a, pb[kb][qb][t], oacc[db][qb], kBf);
   };
-  auto qk_op = [&](int i, u32x4 a) __attribute__((always_inline)) {
+  auto qk_op = [&](int i, Ops o) __attribute__((always_inline)) {
     const int kb = i % S::kKB, st = i / S::kKB;
 #pragma unroll
-    for (int qb = 0; qb < S::kQB; ++qb) sacc[kb][qb] = mfma16(a, q16[qb][st], st == 0 ? f32x16{} : sacc[kb][qb], kBf);
+    for (int qb = 0; qb < S::kQB; ++qb)
+      sacc[kb][qb] = mfma16(o.a, kQ1Lds && qb == 1 ? o.q1 : q16[qb][st], st == 0 ? f32x16{} : sacc[kb][qb], kBf);
   };
   auto pv_rd = [&](const char* lv, int i) __attribute__((always_inline)) {
-    return v_read16(lv, i % S::kDB, i / (2 * S::kDB), (i / S::kDB) % 2);
+    return Ops{v_read16(lv, i % S::kDB, i / (2 * S::kDB), (i / S::kDB) % 2), u32x4{}};
   };
-  auto qk_rd = [&](const char* lk, int i) __attribute__((always_inline)) { return k_read16(lk, i % S::kKB, i / S::kKB); };
+  auto qk_rd = [&](const char* lk, int i) __attribute__((always_inline)) {
+    const int st = i / S::kKB;
+    return Ops{k_read16(lk, i % S::kKB, st), kQ1Lds ? lds_read_b128(lds_q1, q1base + 32 * st) : u32x4{}};
+  };
   auto mfma_phase = [&](int kt, const char* lk, const char* lv_prev) __attribute__((always_inline)) {
     __builtin_amdgcn_s_setprio(1);
     const bool a_pv = active(kt - 1), a_qk = active(kt);
@@ -557,20 +585,20 @@ __global__ __launch_bounds__(NW * 64, WPE) void fa_fwd_kernel(FwdParams p) {
       if (a_pv) pv_interleaved(lv_prev);
       if (a_qk) qk_interleaved(lk);
     } else if (a_pv && a_qk) {
-      op_pipeline<kNPV + kNQK, kNPV, kDepth, S::kQB>(
+      op_pipeline<kNPV + kNQK, kNPV, kDepth, S::kQB, kQKReads>(
           [&](int i) __attribute__((always_inline)) { return i < kNPV ? pv_rd(lv_prev, i) : qk_rd(lk, i - kNPV); },
-          [&](int i, u32x4 a) __attribute__((always_inline)) {
+          [&](int i, Ops o) __attribute__((always_inline)) {
             if (i < kNPV)
-              pv_op(i, a);
+              pv_op(i, o);
             else
-              qk_op(i - kNPV, a);
+              qk_op(i - kNPV, o);
           });
     } else if (a_pv) {
       op_pipeline<kNPV, kNPV, kDepth, S::kQB>([&](int i) __attribute__((always_inline)) { return pv_rd(lv_prev, i); },
-                                      [&](int i, u32x4 a) __attribute__((always_inline)) { pv_op(i, a); });
+                                      [&](int i, Ops o) __attribute__((always_inline)) { pv_op(i, o); });
     } else if (a_qk) {
-      op_pipeline<kNQK, 0, kDepth, S::kQB>([&](int i) __attribute__((always_inline)) { return qk_rd(lk, i); },
-                                   [&](int i, u32x4 a) __attribute__((always_inline)) { qk_op(i, a); });
+      op_pipeline<kNQK, 0, kDepth, S::kQB, kQKReads>([&](int i) __attribute__((always_inline)) { return qk_rd(lk, i); },
+                                   [&](int i, Ops o) __attribute__((always_inline)) { qk_op(i, o); });
     }
     __builtin_amdgcn_s_setprio(0);
   };
@@ -683,15 +711,26 @@ hipError_t launch_one(const FwdParams& p, hipStream_t stream) {
 // value falls back to the default).  Dropout kernels exist for the default
 // shapes only, so FA_TILE is ignored with dropout.
 constexpr Variant kVariants[] = {{32, 8, 64, 1, 2}, {32, 4, 64, 0, 4}, {32, 4, 64, 0, 3}, {32, 4, 64, 0, 2},
-                                 {64, 4, 64, 0, 2}, {64, 8, 64, 1, 2}, {32, 16, 64, 1, 4}, {32, 8, 64, 0, 4}};
+                                 {64, 4, 64, 0, 2}, {64, 8, 64, 1, 2}, {32, 16, 64, 1, 4}, {32, 8, 64, 0, 4},
+                                 {64, 8, 32, 1, 2}};
 // Shapes compiled for d = 64 only (at d = 128 they would spill).
 constexpr bool d64_only(int v) { return v == 5 || v == 6 || v == 7; }
+// Shapes compiled for d = 128 only.
+constexpr bool d128_only(int v) { return v == 8; }
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
 // Measured on MI355X (tile sweep under rocprofv3, interleaved A/B runs in one
-// process): at d = 128 the ping-pong schedule wins for 16-bit types (fp8,
-// with half the operand bytes, prefers the plain schedule at two waves per
-// SIMD).  At d = 64 the softmax's vector work per tile is as long as the
+// process): at d = 128 the ping-pong schedule wins for 16-bit types.  Its
+// matrix phase is bound by the LDS operand reads (1 KB per instruction of a
+// 32-row wave).  64-row waves with 32-key tiles cut them (to half for fp8,
+// whose Q operands fit in registers, and to three quarters at 16 bits, whose
+// second query block's Q operands are read from LDS): without the causal
+// mask +11 % for fp8 and +7 to +8 % for bfloat16 (B8 H32 N4096 / N8192, B4
+// H32 N8192); binary16, whose softmax phase is shorter, gains nothing and
+// keeps 32-row waves.  With the causal mask the 512-row workgroups wait on
+// their longest waves: bfloat16 gains only at N = 16384 (+5 %, against a tie
+// at 8192 and -4 % at 4096), and fp8 keeps the plain schedule at two waves
+// per SIMD.  At d = 64 the softmax's vector work per tile is as long as the
 // tile's matrix work, and a single wave issues vector instructions at well
 // under the SIMD's rate, so the shapes that keep more waves in their softmax
 // at once win: 32 rows per wave at four waves per SIMD.  Without a causal
@@ -703,13 +742,17 @@ constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 // 64-row shape, both by a few percent.  With the causal mask the 4-wave
 // workgroups win: a workgroup waits for its longest wave, and the causal
 // row lengths differ more across 256 rows.  Packed batches of mixed lengths
-// (N = the longest) keep 128-row workgroups for 16-bit types: larger ones
+// (N = the longest) keep 128-row workgroups: larger ones
 // idle most of their waves on the short sequences (lengths 256..4096: 660
 // against 596 TFLOP/s at d = 64, 726 against 699 at d = 128).  Dropout
 // kernels exist for the shapes listed in dispatch_dropout.
 int default_variant(Dtype dt, int d, bool causal, int N, bool dropout, bool packed) {
-  if (packed && !dropout && dt != Dtype::FP8) return d == 128 ? 3 : 1;
-  if (d == 128) return dt == Dtype::FP8 ? 3 : 0;  // plain at two waves per SIMD for fp8, else ping-pong
+  if (packed && !dropout) return d == 128 ? 3 : dt == Dtype::FP8 ? 2 : 1;
+  if (d == 128) {
+    if (dropout) return 0;  // the one d = 128 shape compiled with dropout
+    if (dt == Dtype::FP8) return causal ? 3 : 8;
+    return dt == Dtype::BF16 && (!causal || N >= 16384) ? 8 : 0;
+  }
   if (dropout) return !causal && N >= 1024 ? 4 : 2;
   if (causal) return dt == Dtype::FP8 ? 2 : 1;
   if (N >= 4096 && dt != Dtype::F16) return dt == Dtype::FP8 ? 4 : 5;
@@ -723,7 +766,8 @@ int selected_variant(Dtype dt, int d, bool causal, int N, bool dropout, bool pac
     if (sscanf(env, "%dx%dx%dx%dx%d", &v.qw, &v.nw, &v.bc, &v.sched, &v.wpe) == 5)
       for (int i = 0; i < kNumVariants; ++i)
         if (kVariants[i].qw == v.qw && kVariants[i].nw == v.nw && kVariants[i].bc == v.bc &&
-            kVariants[i].sched == v.sched && kVariants[i].wpe == v.wpe && (!d64_only(i) || d == 64))
+            kVariants[i].sched == v.sched && kVariants[i].wpe == v.wpe && (!d64_only(i) || d == 64) &&
+            (!d128_only(i) || d == 128))
           return i;
   }
   return default_variant(dt, d, causal, N, dropout, packed);
@@ -746,6 +790,9 @@ hipError_t dispatch_variant(int v, const FwdParams& p, hipStream_t stream) {
       return hipErrorInvalidValue;
     case 7:
       if constexpr (D == 64) return launch_one<Tr, D, CAUSAL, 32, 8, 64, 0, 4, false>(p, stream);
+      return hipErrorInvalidValue;
+    case 8:
+      if constexpr (D == 128) return launch_one<Tr, D, CAUSAL, 64, 8, 32, 1, 2, false>(p, stream);
       return hipErrorInvalidValue;
     default: return launch_one<Tr, D, CAUSAL, 32, 8, 64, 1, 2, false>(p, stream);
   }

@@ -125,8 +125,11 @@ def main(argv=None):
     results = []
     for w in args.workloads:
         for t in tiles:
-            if t in ("64x8x64x1x2", "32x16x64x1x4", "32x8x64x0x4") and int(w.split(",")[3]) != 64:
-                continue  # 64-row ping-pong waves are compiled for d = 64 only
+            d = int(w.split(",")[3])
+            if t in ("64x8x64x1x2", "32x16x64x1x4", "32x8x64x0x4") and d != 64:
+                continue  # shapes compiled for d = 64 only
+            if t == "64x8x32x1x2" and d != 128:
+                continue  # compiled for d = 128 only
             with tempfile.TemporaryDirectory(dir="/tmp") as wd:
                 r = measure(t, w, wd)
             print(json.dumps(r), flush=True)

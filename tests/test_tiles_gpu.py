@@ -18,7 +18,7 @@ from tests import gpu_util as gu
 
 pytestmark = pytest.mark.gpu
 
-TILES = ["32x8x64x1x2", "32x4x64x0x4", "32x4x64x0x3", "32x4x64x0x2", "64x4x64x0x2", "64x8x64x1x2", "32x16x64x1x4", "32x8x64x0x4"]
+TILES = ["32x8x64x1x2", "32x4x64x0x4", "32x4x64x0x3", "32x4x64x0x2", "64x4x64x0x2", "64x8x64x1x2", "32x16x64x1x4", "32x8x64x0x4", "64x8x32x1x2"]
 
 
 @pytest.fixture(scope="module", autouse=True)
