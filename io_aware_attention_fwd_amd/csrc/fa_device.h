@@ -117,15 +117,16 @@ __device__ __forceinline__ float halves_sum(float x) {
   return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
 }
 
-// acc + p0 + p1 for the row sum.  binary16 sums the rounded pair with one
-// v_dot2c_f32_f16 (rounding moves the sum by at most 2^-11 relative, well
-// inside the lse bar, and matches the values that enter P V).  bfloat16's
-// 2^-8 rounding would be too coarse for lse, so its sum uses the float32
-// values.
+// acc + p0 + p1 for the row sum.  PACKED sums the binary16-rounded pair with
+// one v_dot2c_f32_f16 (rounding moves the sum by at most 2^-11 relative, well
+// inside the lse bar, and matches the values that enter P V): half the
+// instructions, but each waits for the pair's conversion, which lengthens a
+// lone wave's dependency chains.  Otherwise the float32 values are summed
+// (always for bfloat16, whose 2^-8 rounding would be too coarse for lse).
 typedef __fp16 fp16x2 __attribute__((ext_vector_type(2)));
-template <bool BF16>
+template <bool PACKED>
 __device__ __forceinline__ float sum_pair(u32 packed, float p0, float p1, float acc) {
-  if (BF16) return acc + (p0 + p1);
+  if (!PACKED) return acc + (p0 + p1);
   const fp16x2 one = {(__fp16)1.0f, (__fp16)1.0f};
   return __builtin_amdgcn_fdot2(__builtin_bit_cast(fp16x2, packed), one, acc, false);
 }

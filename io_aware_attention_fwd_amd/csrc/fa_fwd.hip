@@ -94,6 +94,11 @@ struct Shape {
 template <class Tr, int D, bool CAUSAL, int QW, int NW, int BC, int SCHED, int WPE, bool DROP>
 __global__ __launch_bounds__(NW * 64, WPE) void fa_fwd_kernel(FwdParams p) {
   constexpr bool PP = SCHED == 1;
+  // Row sums of binary16 probabilities from the packed pairs only where
+  // several independent waves of a SIMD run their softmax at once (plain
+  // schedule, no causal mask): measured faster there, slower in the lone
+  // softmax wave of the ping-pong schedule and with the causal mask.
+  constexpr bool kPackedSum = !Tr::kPvBf16 && !PP && !CAUSAL;
   static_assert(!PP || NW == 8 || NW == 16, "the ping-pong schedule splits the waves into two groups that each hold NW/8 waves of every SIMD");
   using S = Shape<Tr, D, QW, NW, BC>;
   constexpr bool kBf = Tr::kPvBf16;
@@ -390,7 +395,7 @@ __global__ __launch_bounds__(NW * 64, WPE) void fa_fwd_kernel(FwdParams p) {
             } else {
               pb[kb][qb][t][e] = w;
             }
-            rs[e] = sum_pair<kBf>(w, p0, p1, rs[e]);
+            rs[e] = sum_pair<kPackedSum>(w, p0, p1, rs[e]);
           }
       }
       tsum[qb] = (rs[0] + rs[1]) + (rs[2] + rs[3]);
@@ -725,9 +730,8 @@ constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 // 32-row wave).  64-row waves with 32-key tiles cut them (to half for fp8,
 // whose Q operands fit in registers, and to three quarters at 16 bits, whose
 // second query block's Q operands are read from LDS): without the causal
-// mask +11 % for fp8 and +7 to +8 % for bfloat16 (B8 H32 N4096 / N8192, B4
-// H32 N8192); binary16, whose softmax phase is shorter, gains nothing and
-// keeps 32-row waves.  With the causal mask the 512-row workgroups wait on
+// mask +11 % for fp8 and +6 to +8 % for the 16-bit types (B8 H32 N4096 /
+// N8192, B4 H32 N8192).  With the causal mask the 512-row workgroups wait on
 // their longest waves: bfloat16 gains only at N = 16384 (+5 %, against a tie
 // at 8192 and -4 % at 4096), and fp8 keeps the plain schedule at two waves
 // per SIMD.  At d = 64 the softmax's vector work per tile is as long as the
@@ -751,7 +755,7 @@ int default_variant(Dtype dt, int d, bool causal, int N, bool dropout, bool pack
   if (d == 128) {
     if (dropout) return 0;  // the one d = 128 shape compiled with dropout
     if (dt == Dtype::FP8) return causal ? 3 : 8;
-    return dt == Dtype::BF16 && (!causal || N >= 16384) ? 8 : 0;
+    return !causal || N >= 16384 ? 8 : 0;
   }
   if (dropout) return !causal && N >= 1024 ? 4 : 2;
   if (causal) return dt == Dtype::FP8 ? 2 : 1;
