@@ -711,10 +711,12 @@ hipError_t launch_one(const FwdParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Tile shapes compiled for every (dtype, d, causal).  FA_TILE=<qw>x<nw>x<bc>x<sched>x<wpe>
-// selects one of them instead of the default (tile sweeps only; an unknown
-// value falls back to the default).  Dropout kernels exist for the default
-// shapes only, so FA_TILE is ignored with dropout.
+// Tile shapes compiled for every (dtype, causal); the first five for both
+// head dimensions, the others for the one d64_only / d128_only name.
+// FA_TILE=<qw>x<nw>x<bc>x<sched>x<wpe> selects one of them instead of the
+// default (tile sweeps only; an unknown value, or a shape not compiled for
+// the call's head dimension, falls back to the default).  Dropout kernels
+// exist for the default shapes only, so FA_TILE is ignored with dropout.
 constexpr Variant kVariants[] = {{32, 8, 64, 1, 2}, {32, 4, 64, 0, 4}, {32, 4, 64, 0, 3}, {32, 4, 64, 0, 2},
                                  {64, 4, 64, 0, 2}, {64, 8, 64, 1, 2}, {32, 16, 64, 1, 4}, {32, 8, 64, 0, 4},
                                  {64, 8, 32, 1, 2}};
