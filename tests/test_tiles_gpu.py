@@ -45,3 +45,23 @@ def test_tile_parity(tile, dtype, d):
             gu.compare(x, gu.o_to_numpy(o), lse.cpu().numpy().astype(np.float64), scale, causal)
     finally:
         os.environ.pop("FA_TILE", None)
+
+
+@pytest.mark.parametrize("tile", TILES)
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", [1, 17, 100])
+def test_tile_short_sequences(tile, d, N):
+    """Lengths below one key tile and one wave's rows: most waves of the
+    workgroup, and all but the first rows of the first, lie past N."""
+    B, H = 2, 3
+    dtype = "f16" if d == 64 else "bf16"
+    print(f"[tile] {tile} {dtype} d={d} N={N}", flush=True)
+    x = gen.make(B, H, N, d, dtype, seed=12)
+    scale = 1 / math.sqrt(d)
+    os.environ["FA_TILE"] = tile
+    try:
+        for causal in (False, True):
+            o, lse = gu.run_gpu(x, scale, causal)
+            gu.compare(x, gu.o_to_numpy(o), lse.cpu().numpy().astype(np.float64), scale, causal)
+    finally:
+        os.environ.pop("FA_TILE", None)
