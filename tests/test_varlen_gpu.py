@@ -16,6 +16,7 @@ import torch
 import oracle
 from io_aware_attention_fwd_amd import _lib, gen
 from tests import gpu_util as gu
+from tests.test_tiles_gpu import TILES  # every compiled tile shape
 
 pytestmark = pytest.mark.gpu
 
@@ -155,3 +156,21 @@ def test_varlen_long_sequences_sampled(d, dtype, causal):
     o, lse = _run(x, cu, max(lengths), scale, causal)
     do, dl = _compare(x, cu, o, lse, scale, causal, sequences=[0, 1, 5], heads=[0, 15])
     print(f"[varlen] max|dO|={do:.3g} max rel dlse={dl:.3g}")
+
+
+# Every compiled tile shape (FA_TILE) on the mixed-length batch: the packed
+# addressing (sequence bounds, empty query tiles, rows past a sequence's end)
+# is shared by all of them.
+@pytest.mark.parametrize("tile", TILES)
+@pytest.mark.parametrize("d,dtype", [(64, "f16"), (128, "bf16")])
+def test_varlen_every_tile(tile, d, dtype):
+    print(f"[varlen] tile {tile} d={d} {dtype}", flush=True)
+    x, cu = gen.make_packed(LENGTHS, 2, d, dtype, seed=13)
+    scale = 1 / math.sqrt(d)
+    os.environ["FA_TILE"] = tile
+    try:
+        for causal in (False, True):
+            o, lse = _run(x, cu, max(LENGTHS), scale, causal)
+            _compare(x, cu, o, lse, scale, causal)
+    finally:
+        os.environ.pop("FA_TILE", None)
