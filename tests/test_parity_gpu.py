@@ -158,7 +158,8 @@ def test_lse_self_consistency_large():
         assert np.abs(w @ v - o_np[b, h, rows]).max() < 1e-2
 
 
-@pytest.mark.parametrize("N,d,dtype,causal", [(131072, 128, "bf16", True), (65536, 64, "f16", False)])
+@pytest.mark.parametrize("N,d,dtype,causal", [(131072, 128, "bf16", True), (65536, 64, "f16", False),
+                                              (32768, 128, "f16", False), (32768, 128, "fp8", False)])
 def test_long_sequences_sampled_rows(N, d, dtype, causal):
     """Long sequences (a 32 MiB slice at N = 131072, d = 128): 24 sampled rows
     per slice, the first and last included, each against the oracle on the
