@@ -5,9 +5,10 @@
 Runs ``bench.py`` under ``rocprofv3`` (each run a child process started from
 /tmp with a time limit) and writes short text summaries into DIR:
 
-* ``<tag>_kernel_stats.md``: ``--kernel-trace --stats`` of the timed bench
-  command (20 steps after 5 warm-ups), the forward kernel's average duration
-  and the TFLOP/s it implies;
+* ``<tag>_kernel_stats.md``: ``--kernel-trace --stats`` of the bench command
+  with its default warm-up and step counts (the same command bench.py's line
+  comes from), the forward kernel's average duration and the TFLOP/s it
+  implies;
 * for the headline workload only (no ``--shape``): ``<tag>_counters.md`` and
   ``<tag>_traffic.json`` from three counter runs, ``--pmc FETCH_SIZE`` and
   ``--pmc WRITE_SIZE`` (one counter per run, each next to a 256 MiB device
@@ -48,8 +49,10 @@ SQ_COUNTERS = ["SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_VALU_MFMA_BUSY_C
                "SQ_ACTIVE_INST_VALU", "SQ_WAVE_CYCLES", "SQ_WAIT_INST_LDS", "GRBM_GUI_ACTIVE"]
 
 
-def _bench_args(shape, steps, warmup, extra=()):
-    args = ["--no-sweep", "--no-cpu", "--steps", str(steps), "--warmup", str(warmup)] + list(extra)
+def _bench_args(shape, steps=None, warmup=None, extra=()):
+    args = ["--no-sweep", "--no-cpu"] + list(extra)
+    if steps is not None:
+        args += ["--steps", str(steps), "--warmup", str(warmup)]
     if shape != HEADLINE:
         B, H, N, d, dt, causal = shape
         args += ["--shape", f"{B},{H},{N},{d},{dt},{int(causal)}"]
@@ -98,7 +101,7 @@ def record(shape, out_dir):
     desc = f"B={B} H={H} N={N} d={d} {dt} " + ("causal" if causal else "non-causal")
 
     with tempfile.TemporaryDirectory(dir="/tmp") as wd:
-        bargs = _bench_args(shape, 20, 5)
+        bargs = _bench_args(shape)
         pargs, line = _profile(["--kernel-trace", "--stats"], bargs, os.path.join(wd, "trace"), "trace")
         stats = glob.glob(os.path.join(wd, "trace", "**", "*_kernel_stats.csv"), recursive=True)[0]
         text = open(stats).read().strip()
@@ -174,7 +177,7 @@ def record(shape, out_dir):
 def record_mode(mode, mode_arg, tag, out_dir):
     """Kernel statistics of bench.py --MODE ARG (one step may launch several kernels)."""
     os.makedirs(out_dir, exist_ok=True)
-    bargs = ["--no-sweep", "--no-cpu", f"--{mode}", mode_arg, "--steps", "10", "--warmup", "3"]
+    bargs = ["--no-sweep", "--no-cpu", f"--{mode}", mode_arg]
     with tempfile.TemporaryDirectory(dir="/tmp") as wd:
         pargs, line = _profile(["--kernel-trace", "--stats"], bargs, os.path.join(wd, "trace"), "trace")
         stats = glob.glob(os.path.join(wd, "trace", "**", "*_kernel_stats.csv"), recursive=True)[0]
