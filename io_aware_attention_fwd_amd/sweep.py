@@ -6,7 +6,9 @@ For every tile variant compiled into libfa.so (the ``kVariants`` table of
 ``csrc/fa_fwd.hip``, selected per call with ``FA_TILE``) and every workload,
 this runs ``bench.py --shape ...`` three times under ``rocprofv3``:
 
-1. ``--kernel-trace --stats``: average kernel duration -> TFLOP/s;
+1. ``--kernel-trace --stats`` with bench.py's default warm-up and step counts
+   (the clock needs tens of milliseconds of load to leave its idle level):
+   average kernel duration -> TFLOP/s;
 2. ``--pmc`` SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE SQ_LDS_BANK_CONFLICT
    SQ_LDS_IDX_ACTIVE: matrix-core utilisation and LDS bank conflicts;
 3. ``--pmc FETCH_SIZE`` and ``--pmc WRITE_SIZE`` (one counter per run), the
@@ -81,8 +83,8 @@ def measure(tile, workload, workdir, timeout=300):
     res = {"tile": tile, "workload": workload}
     # 1. duration
     out = os.path.join(workdir, "trace")
-    _run(_rocprof(["--kernel-trace", "--stats"], out, "t", env, timeout) + shape + ["--steps", "10", "--warmup", "3"],
-         env, timeout)
+    # bench.py's default warm-up and steps, so the clock has left its idle level
+    _run(_rocprof(["--kernel-trace", "--stats"], out, "t", env, timeout) + shape, env, timeout)
     rows = [r for f in glob.glob(os.path.join(out, "*_kernel_stats.csv")) for r in csv.DictReader(open(f))
             if "fa_fwd_kernel" in r["Name"]]
     avg_ns = float(rows[0]["AverageNs"])
