@@ -6,8 +6,10 @@ Prints ONE JSON line.  A step is one ``fa_fwd`` call (the whole forward pass:
 Q tile load, K/V streaming, Q K^T, mask, online softmax, P V, epilogue) on
 B=8, H=32, N=1024, d=64 binary16 inputs, non-causal, scale 1/8, drawn i.i.d.
 N(0,1) from seed 0.  Inputs are resident in device memory before the timed
-region; K steps are timed with HIP events on the stream the kernel runs on,
-between two device synchronisations.
+region; after W untimed warm-up steps (500 by default: the shader clock needs
+tens of milliseconds of load to leave its idle level), K steps (200 by
+default) are timed with HIP events on the stream the kernel runs on, between
+two device synchronisations.
 
 Throughput is 4*B*H*N^2*d FLOP per step (halved for causal) / time.  The line
 also carries per-call median / min / p90 times, the sequence-length sweep
