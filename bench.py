@@ -14,7 +14,9 @@ two device synchronisations.
 Throughput is 4*B*H*N^2*d FLOP per step (halved for causal) / time.  The line
 also carries per-call median / min / p90 times, the sequence-length sweep
 N = 512..8192 at B=8, H=32, d=64 (the shape of the benchmark page's
-forward-time tables) plus d=128 and causal points at N >= 4096, the shader and
+forward-time tables) plus d=128 and causal points at N >= 4096 and the fp8
+(B8 H32 N8192 d64) and long-sequence (B2 H16 N16384 d128 bf16 causal)
+configurations, each after a 50 ms warm-up of its own, the shader and
 memory clock levels in use under load, the fraction of the dense
 fp16 matrix-core peak, HBM traffic from committed rocprofv3 counters when they
 were taken on the current kernel source, and the CPU oracle timed on a bounded
@@ -379,21 +381,24 @@ def main(argv=None):
     clocks = None
     if not args.no_sweep and not args.shape:
         # the benchmark page's forward-time tables: B=8, H=32, d=64, N=512..8192, no mask
-        points = [(n, 64, dtype, False) for n in (512, 1024, 2048, 4096, 8192)]
+        points = [(B, H, n, 64, dtype, False) for n in (512, 1024, 2048, 4096, 8192)]
         # the >=4096 head-dimension 64/128 cases, also causal and bfloat16
-        points += [(4096, 64, "bf16", True), (8192, 64, "bf16", True), (4096, 128, "f16", False),
-                   (8192, 128, "bf16", False), (8192, 128, "bf16", True)]
+        points += [(B, H, 4096, 64, "bf16", True), (B, H, 8192, 64, "bf16", True), (B, H, 4096, 128, "f16", False),
+                   (B, H, 8192, 128, "bf16", False), (B, H, 8192, 128, "bf16", True)]
+        # the fp8 configuration (B8 H32 N8192 d64, bfloat16 O) and the long-sequence one (B2 H16 N16384 d128
+        # bfloat16 causal)
+        points += [(B, H, 8192, 64, "fp8", False), (2, 16, 16384, 128, "bf16", True)]
         inputs = {}
-        for n, dd, dt, cz in points:
-            progress(f"sweep point N={n} d={dd} {dt} causal={int(cz)}")
-            if (n, dd, dt) not in inputs:  # causal and non-causal points share one input draw
-                inputs = {(n, dd, dt): None}
-            c2, st2, keep2 = make_call(B, H, n, dd, dt, cz, 1.0 / math.sqrt(dd), x=inputs[(n, dd, dt)])
-            inputs[(n, dd, dt)] = keep2[0]
+        for pb, ph, n, dd, dt, cz in points:
+            progress(f"sweep point B={pb} H={ph} N={n} d={dd} {dt} causal={int(cz)}")
+            if (pb, ph, n, dd, dt) not in inputs:  # causal and non-causal points share one input draw
+                inputs = {(pb, ph, n, dd, dt): None}
+            c2, st2, keep2 = make_call(pb, ph, n, dd, dt, cz, 1.0 / math.sqrt(dd), x=inputs[(pb, ph, n, dd, dt)])
+            inputs[(pb, ph, n, dd, dt)] = keep2[0]
             reps = 20 if n >= 4096 else 50
             warm(c2)
-            r = summarize(time_each(c2, 0, reps, st2), flops(B, H, n, dd, cz), PEAK_TFLOPS[dt])
-            sweep.append({"N": n, "d": dd, "dtype": dt, "causal": cz, **r})
+            r = summarize(time_each(c2, 0, reps, st2), flops(pb, ph, n, dd, cz), PEAK_TFLOPS[dt])
+            sweep.append({"B": pb, "H": ph, "N": n, "d": dd, "dtype": dt, "causal": cz, **r})
             if clocks is None and n == 8192:
                 def busy(c=c2):
                     for _ in range(30):
