@@ -6,21 +6,26 @@ Prints ONE JSON line.  A step is one ``fa_fwd`` call (the whole forward pass:
 Q tile load, K/V streaming, Q K^T, mask, online softmax, P V, epilogue) on
 B=8, H=32, N=1024, d=64 binary16 inputs, non-causal, scale 1/8, drawn i.i.d.
 N(0,1) from seed 0.  Inputs are resident in device memory before the timed
-region; after W untimed warm-up steps (500 by default: the shader clock needs
-tens of milliseconds of load to leave its idle level), K steps (200 by
-default) are timed with HIP events on the stream the kernel runs on, between
-two device synchronisations.
+region.  The shader clock needs tens of milliseconds of load to leave its
+idle level, so the GPU is first kept busy with plain device matmuls
+(``--clock-ms``, 100 by default; not the benchmarked call); then come W
+untimed warm-up steps (500 by default) and K timed steps (200 by default),
+timed with HIP events on the stream the kernel runs on, between two device
+synchronisations.
 
 Throughput is 4*B*H*N^2*d FLOP per step (halved for causal) / time.  The line
-also carries per-call median / min / p90 times, the sequence-length sweep
-N = 512..8192 at B=8, H=32, d=64 (the shape of the benchmark page's
-forward-time tables) plus d=128 and causal points at N >= 4096 and the fp8
-(B8 H32 N8192 d64) and long-sequence (B2 H16 N16384 d128 bf16 causal)
-configurations, each after a 50 ms warm-up of its own, the shader and
-memory clock levels in use under load, the fraction of the dense
-fp16 matrix-core peak, HBM traffic from committed rocprofv3 counters when they
-were taken on the current kernel source, and the CPU oracle timed on a bounded
-sample of the same workload.
+also carries per-call median / min / p90 times; the five configurations
+(B1 H2 N128 d64 f16; B8 H32 N1024 d64 f16; B8 H32 N4096 d64 bf16 causal;
+B8 H32 N8192 d64 fp8 in, bf16 out; B2 H16 N16384 d128 bf16 causal) as
+entries of their own, each with its fraction of the dtype's dense
+matrix-core peak, algorithmic HBM GB/s, HBM traffic from committed
+rocprofv3 counters when they were taken on the current kernel source, the
+LDS and vector-ALU ceilings, and the float64 CPU oracle timed on the host
+cores (in full where that takes seconds, else on sampled (b, h) slices,
+extrapolated); the sequence-length sweep N = 512..8192 at B=8, H=32, d=64
+(the shape of the benchmark page's forward-time tables) plus d=128 and
+causal points at N >= 4096, each after a 50 ms warm-up of its own; and the
+shader and memory clock levels in use under load.
 
 Other modes print one line each for the other entry points instead of the
 headline: ``--shape`` (another dense forward shape), ``--varlen`` (packed
@@ -43,8 +48,24 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "fp8": 5000.0}  # MI355X dense matrix-core peaks
 HBM_PEAK_GBS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_f16_b8h32n1024d64_traffic.json")
-KERNEL_SOURCES = [os.path.join(ROOT, "io_aware_attention_fwd_amd", "csrc", f) for f in ("fa_fwd.hip", "fa_device.h", "fa_launch.h")]
+CLOCK_GHZ = 2.4          # the clock the MI355X peaks are quoted at
+N_CU = 256
+LDS_BYTES_PER_CLK = 128  # LDS read bandwidth per CU assumed for the LDS ceiling (CDNA3's documented figure)
+PROFILES = os.path.join(ROOT, "profiles")
+TRAFFIC_FILE = os.path.join(PROFILES, "fa_fwd_f16_b8h32n1024d64_traffic.json")
+_CSRC = os.path.join(ROOT, "io_aware_attention_fwd_amd", "csrc")
+# the sources each kernel family is built from (a profile is current while their hash is unchanged)
+KERNEL_FAMILIES = {
+    "fwd": ["fa_fwd.hip", "fa_device.h", "fa_launch.h", "fa_variants.h"],
+    "bwd": ["fa_bwd.hip", "fa_device.h", "fa_launch.h"],
+    "proj": ["fa_proj.hip", "fa_device.h", "fa_launch.h"],
+}
+KERNEL_SOURCES = [os.path.join(_CSRC, f) for f in KERNEL_FAMILIES["fwd"]]
+
+# The five configurations of the benchmark: (tag, B, H, N, d, dtype, causal); scale 1/sqrt(d).
+CONFIGS = [("c1", 1, 2, 128, 64, "f16", False), ("c2", 8, 32, 1024, 64, "f16", False),
+           ("c3", 8, 32, 4096, 64, "bf16", True), ("c4", 8, 32, 8192, 64, "fp8", False),
+           ("c5", 2, 16, 16384, 128, "bf16", True)]
 
 
 def flops(B, H, N, d, causal):
@@ -57,12 +78,64 @@ def algorithmic_bytes(B, H, N, d, in_bytes, out_bytes):
     return (3 * in_bytes + out_bytes) * B * H * N * d + 4 * B * H * N
 
 
-def kernel_source_hash():
+def kernel_source_hash(family="fwd"):
+    """Hash of the sources one kernel family is built from ("fwd", "bwd" or "proj")."""
+    paths = KERNEL_SOURCES if family == "fwd" else [os.path.join(_CSRC, f) for f in KERNEL_FAMILIES[family]]
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in paths:
         with open(p, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def record_tag(B, H, N, d, dtype, causal):
+    """File stem of a forward workload's profiles under profiles/."""
+    return f"fa_fwd_{dtype}_b{B}h{H}n{N}d{d}" + ("_causal" if causal else "")
+
+
+def load_record(tag):
+    """The committed rocprofv3 counter record of a workload, if it was taken on the current kernel source."""
+    path = TRAFFIC_FILE if tag == record_tag(8, 32, 1024, 64, "f16", False) else os.path.join(PROFILES, f"{tag}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return t
+
+
+def lds_bytes_per_score(d, dtype, tile):
+    """LDS operand bytes one score costs with the tile shape (QWxNWxBCxSCHEDxWPE) that runs: each wave
+    reads the whole K and V tile once per tile for its QW query rows (and, with 64-row waves at d = 128
+    and 16-bit values, its second 32-row block's Q operands)."""
+    qw, _, bc = (int(x) for x in tile.split("x")[:3])
+    e = 1 if dtype == "fp8" else 2
+    b = d * 2 * e / qw
+    if qw == 64 and d == 128 and dtype != "fp8":
+        b += 32 * d * 2 / (qw * bc)
+    return b
+
+
+def secondary_ceilings(d, dtype, causal, fl, tile, rec):
+    """Ceilings other than the matrix cores, in TFLOP/s at the quoted 2.4 GHz: the LDS operand reads
+    (from the tile shape) and, where the counter record holds instruction counts, the vector ALU issue
+    (4 cycles per wave64 instruction, 8 for an exponential or logarithm) per launch."""
+    out = {"lds_bytes_per_score": round(lds_bytes_per_score(d, dtype, tile), 3),
+           "lds_ceiling_tflops": round(N_CU * LDS_BYTES_PER_CLK * CLOCK_GHZ * 1e9 / lds_bytes_per_score(d, dtype, tile)
+                                       * 4 * d / 1e12, 1),
+           "lds_assumption": f"{LDS_BYTES_PER_CLK} B/clk per CU, {N_CU} CUs, {CLOCK_GHZ} GHz"}
+    counts = (rec or {}).get("instructions")
+    if counts and counts.get("valu") is not None:
+        trans = counts.get("valu_trans") or 0
+        other = counts["valu"] - trans - (counts.get("mfma") or 0)
+        cycles = 4 * other + 8 * trans
+        t = cycles / (4 * N_CU) / (CLOCK_GHZ * 1e9)
+        scores = fl / (4 * d)
+        out.update({"valu_insts_per_score": round(64 * other / scores, 3),
+                    "trans_insts_per_score": round(64 * trans / scores, 3),
+                    "valu_ceiling_tflops": round(fl / t / 1e12, 1)})
+    return out
 
 
 def progress(msg):
@@ -99,6 +172,24 @@ def warm(fn, seconds=0.05):
         torch.cuda.synchronize()
         if time.perf_counter() - t0 >= seconds:
             return
+
+
+def condition_clock(ms):
+    """Keep the GPU busy with plain device matmuls (not the benchmarked call) for about ``ms``
+    milliseconds: the shader clock needs tens of milliseconds of load to leave its idle level, and
+    a timed region of a few milliseconds that starts on an idle clock reads ~20 % low."""
+    import torch
+
+    if ms <= 0:
+        return
+    a = torch.randn(2048, 2048, device="cuda", dtype=torch.float16)
+    b = torch.empty_like(a)
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(8):
+            torch.mm(a, a, out=b)
+        torch.cuda.synchronize()
+    del a, b
 
 
 def time_each(fn, warmup, steps, stream):
@@ -229,18 +320,30 @@ def make_call_varlen(lengths, H, d, dtype, causal, scale, seed=0):
     return call, stream, (x, cu, q, k, v, o, lse, cu_t)
 
 
+def oracle_threads():
+    """BLAS threads for the oracle: the CPUs this process may run on (sched_getaffinity), capped by
+    OMP_NUM_THREADS where the host sets it to its share; returns the count actually in use."""
+    n = len(os.sched_getaffinity(0))
+    cap = os.environ.get("OMP_NUM_THREADS")
+    if cap and cap.isdigit() and int(cap) > 0:
+        n = min(n, int(cap))
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+
+        threadpool_limits(limits=n, user_api="blas")
+        used = [p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"]
+        return max(used) if used else n
+    except Exception:  # pragma: no cover
+        return n
+
+
 def cpu_baseline_varlen(x, cu, causal, scale, budget_s):
     """The float64 oracle on (sequence, head) slices of a packed batch for about
     ``budget_s`` seconds, extrapolated to the whole batch by FLOPs."""
     import oracle
 
     H, d = x.q.shape[1], x.q.shape[2]
-    try:
-        from threadpoolctl import threadpool_info
-
-        cores = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
-    except Exception:  # pragma: no cover
-        cores = None
+    cores = oracle_threads()
     lengths = np.diff(cu)
     total_fl = sum(flops(1, H, int(n), d, causal) for n in lengths)
     done_fl, n_slices, t0 = 0.0, 0, time.perf_counter()
@@ -270,12 +373,7 @@ def cpu_baseline(x, causal, scale, budget_s):
 
     B, H, N, d = x.shape
     dtype = x.dtype
-    try:
-        from threadpoolctl import threadpool_info
-
-        cores = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
-    except Exception:  # pragma: no cover
-        cores = None
+    cores = oracle_threads()
     done, t0 = 0, time.perf_counter()
     while True:
         b, h = divmod(done % (B * H), H)
@@ -294,15 +392,34 @@ def cpu_baseline(x, causal, scale, budget_s):
                       f"({full_s * 1e3:.0f} ms per step)"}
 
 
+def cpu_baseline_sampled(x, causal, scale, budget_s, slices):
+    """The float64 oracle on the given (b, h) slices, in order, until ``budget_s`` seconds have passed
+    (at least one slice), extrapolated to all B*H slices: the whole workload takes hours of host time
+    at N >= 4096, so only a bounded sample is timed."""
+    import oracle
+
+    B, H, N, d = x.shape
+    cores = oracle_threads()
+    done, t0 = 0, time.perf_counter()
+    for b, h in slices:
+        qkv = [oracle.dequantize(a[b, h], x.dtype, x.descale[n]) for a, n in ((x.q, "q"), (x.k, "k"), (x.v, "v"))]
+        oracle.attention_slice(qkv[0], qkv[1], qkv[2], scale, causal)
+        done += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    el = time.perf_counter() - t0
+    full_s = el / done * B * H
+    return {"value": flops(B, H, N, d, causal) / full_s / 1e12, "unit": "TFLOPS", "cores": cores, "kind": "oracle",
+            "ms_per_step_extrapolated": round(full_s * 1e3, 1),
+            "sample": f"{done} of the sampled (b,h) slices {slices[:done]} of N={N}, d={d} ({x.dtype} inputs, float64 "
+                      f"math) timed in {el:.1f} s; the {B * H} slices extrapolated x{B * H / done:g} to "
+                      f"{full_s:.1f} s per step"}
+
+
 def load_traffic(_unused=None):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if current."""
-    if not os.path.exists(TRAFFIC_FILE):
-        return None
-    with open(TRAFFIC_FILE) as f:
-        t = json.load(f)
-    if t.get("kernel_source_sha256_16") != kernel_source_hash():
-        return None
-    return t.get("bytes_per_launch")
+    """HBM bytes per launch of the headline workload from the committed rocprofv3 counter record, if current."""
+    t = load_record(record_tag(8, 32, 1024, 64, "f16", False))
+    return None if t is None else t.get("bytes_per_launch")
 
 
 def main(argv=None):
@@ -314,7 +431,10 @@ def main(argv=None):
     # calls the timed region starts before the clock has ramped and the
     # headline reads ~20 % low; 500 and 2000 warm-up calls agree within 1 %.
     ap.add_argument("--warmup", type=int, default=500)
-    ap.add_argument("--no-sweep", action="store_true", help="skip the N=512..8192 sweep")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the configurations and the N=512..8192 sweep")
+    ap.add_argument("--clock-ms", type=float, default=100.0,
+                    help="milliseconds of device matmuls before the warm-up calls, to bring the shader clock "
+                         "up from idle (0: none)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the CPU baseline")
     ap.add_argument("--shape", default=None,
@@ -370,6 +490,7 @@ def main(argv=None):
         b.copy_(a)
         torch.cuda.synchronize()
         del a, b
+    condition_clock(args.clock_ms)
     ms = time_calls(call, args.warmup, args.steps, stream)
     fl = flops(B, H, N, d, causal)
     peak = PEAK_TFLOPS[dtype]
@@ -377,35 +498,66 @@ def main(argv=None):
     tflops = fl / (ms * 1e-3) / 1e12
     algo_bytes = algorithmic_bytes(B, H, N, d, 1 if dtype == "fp8" else 2, 2)
 
-    sweep = []
+    from io_aware_attention_fwd_amd import _lib
+
+    def point(pb, ph, n, dd, dt, cz, x=None):
+        """Time one workload (after a 50 ms warm-up of its own); returns (entry, inputs)."""
+        c2, st2, keep2 = make_call(pb, ph, n, dd, dt, cz, 1.0 / math.sqrt(dd), x=x)
+        warm(c2)
+        fl2 = flops(pb, ph, n, dd, cz)
+        r = summarize(time_each(c2, 0, 20 if n >= 4096 else 50, st2), fl2, PEAK_TFLOPS[dt])
+        ab = algorithmic_bytes(pb, ph, n, dd, 1 if dt == "fp8" else 2, 2)
+        tile = _lib.fwd_tile(n, dd, cz, {"f16": 0, "bf16": 1, "fp8": 2}[dt])
+        e = {"B": pb, "H": ph, "N": n, "d": dd, "dtype": dt, "causal": cz, "tile": tile, **r,
+             "peak_tflops": PEAK_TFLOPS[dt], "algorithmic_bytes": ab,
+             "algorithmic_hbm_gbs": round(ab / (r["ms_median"] * 1e-3) / 1e9, 1)}
+        return e, keep2[0], c2
+
+    configs, sweep = [], []
     clocks = None
     if not args.no_sweep and not args.shape:
-        # the benchmark page's forward-time tables: B=8, H=32, d=64, N=512..8192, no mask
-        points = [(B, H, n, 64, dtype, False) for n in (512, 1024, 2048, 4096, 8192)]
-        # the >=4096 head-dimension 64/128 cases, also causal and bfloat16
-        points += [(B, H, 4096, 64, "bf16", True), (B, H, 8192, 64, "bf16", True), (B, H, 4096, 128, "f16", False),
-                   (B, H, 8192, 128, "bf16", False), (B, H, 8192, 128, "bf16", True)]
-        # the fp8 configuration (B8 H32 N8192 d64, bfloat16 O) and the long-sequence one (B2 H16 N16384 d128
-        # bfloat16 causal)
-        points += [(B, H, 8192, 64, "fp8", False), (2, 16, 16384, 128, "bf16", True)]
-        inputs = {}
-        for pb, ph, n, dd, dt, cz in points:
-            progress(f"sweep point B={pb} H={ph} N={n} d={dd} {dt} causal={int(cz)}")
-            if (pb, ph, n, dd, dt) not in inputs:  # causal and non-causal points share one input draw
-                inputs = {(pb, ph, n, dd, dt): None}
-            c2, st2, keep2 = make_call(pb, ph, n, dd, dt, cz, 1.0 / math.sqrt(dd), x=inputs[(pb, ph, n, dd, dt)])
-            inputs[(pb, ph, n, dd, dt)] = keep2[0]
-            reps = 20 if n >= 4096 else 50
-            warm(c2)
-            r = summarize(time_each(c2, 0, reps, st2), flops(pb, ph, n, dd, cz), PEAK_TFLOPS[dt])
-            sweep.append({"B": pb, "H": ph, "N": n, "d": dd, "dtype": dt, "causal": cz, **r})
-            if clocks is None and n == 8192:
+        # the five configurations, each a first-class entry with its own roofline figures and oracle baseline
+        for tag, pb, ph, n, dd, dt, cz in CONFIGS:
+            progress(f"config {tag} B={pb} H={ph} N={n} d={dd} {dt} causal={int(cz)}")
+            e, x2, c2 = point(pb, ph, n, dd, dt, cz)
+            fl2 = flops(pb, ph, n, dd, cz)
+            rec = load_record(record_tag(pb, ph, n, dd, dt, cz))
+            e = {"config": tag, **e,
+                 "hbm_traffic_bytes": None if rec is None else rec.get("bytes_per_launch"),
+                 "hbm_traffic_ratio_to_algorithmic": None if rec is None else rec.get("ratio_to_algorithmic"),
+                 "secondary_ceilings": secondary_ceilings(dd, dt, cz, fl2, e["tile"], rec)}
+            if dt == "fp8":
+                # P V runs on bfloat16 matrix instructions (fp8 Q K^T), so the dtype's own ceiling is the
+                # harmonic mix of the two peaks over equal halves of the FLOPs
+                e["mixed_peak_tflops"] = round(2 / (1 / PEAK_TFLOPS["fp8"] + 1 / PEAK_TFLOPS["bf16"]), 1)
+                e["frac_of_mixed_peak"] = round(e["tflops"] / e["mixed_peak_tflops"], 4)
+            if clocks is None and n >= 4096:
                 def busy(c=c2):
                     for _ in range(30):
                         c()
                 clocks = gpu_clock_state(busy)
                 torch.cuda.synchronize()
-            del keep2
+            if not args.no_cpu:
+                progress(f"config {tag}: cpu baseline (oracle)")
+                if pb * ph * n <= 8 * 32 * 1024:
+                    e["cpu_baseline"] = cpu_baseline(x2, cz, 1.0 / math.sqrt(dd), args.cpu_budget / 3)
+                else:
+                    import oracle
+
+                    e["cpu_baseline"] = cpu_baseline_sampled(x2, cz, 1.0 / math.sqrt(dd), args.cpu_budget / 3,
+                                                             oracle.slice_sample(pb, ph))
+            configs.append(e)
+            del x2, c2
+            torch.cuda.empty_cache()
+        # the benchmark page's forward-time table shape (B=8, H=32, d=64, N=512..8192, no mask) and the
+        # N >= 4096 head-dimension 64/128 points, causal and bfloat16 too (c2 and c4 are entries above)
+        points = [(B, H, n, 64, dtype, False) for n in (512, 2048, 4096, 8192)]
+        points += [(B, H, 8192, 64, "bf16", True), (B, H, 4096, 128, "f16", False),
+                   (B, H, 8192, 128, "bf16", False), (B, H, 8192, 128, "bf16", True)]
+        for pb, ph, n, dd, dt, cz in points:
+            progress(f"sweep point B={pb} H={ph} N={n} d={dd} {dt} causal={int(cz)}")
+            e, _, _ = point(pb, ph, n, dd, dt, cz)
+            sweep.append(e)
             torch.cuda.empty_cache()
     if clocks is None:
         def busy():
@@ -414,7 +566,8 @@ def main(argv=None):
         clocks = gpu_clock_state(busy)
         torch.cuda.synchronize()
 
-    traffic = load_traffic(None) if not args.shape else None
+    rec = load_record(record_tag(B, H, N, d, dtype, causal))
+    traffic = None if rec is None else rec.get("bytes_per_launch")
     line = {
         "metric": "attention fwd TFLOPS + ms at B=8,H=32,d=64,N=512..8192; % of MFMA peak",
         "value": round(tflops, 2),
@@ -431,14 +584,20 @@ def main(argv=None):
         "data": f"synthetic: i.i.d. N(0,1) inputs from seed 0, stored as {dtype}",
         "config": {"workload": f"attention forward B={B} H={H} N={N} d={d} {dtype} "
                                f"{'causal' if causal else 'non-causal'} scale=1/sqrt({d})",
-                   "B": B, "H": H, "N": N, "d": d, "causal": causal},
+                   "B": B, "H": H, "N": N, "d": d, "causal": causal,
+                   "tile": _lib.fwd_tile(N, d, causal, {"f16": 0, "bf16": 1, "fp8": 2}[dtype])},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(tflops / peak, 4), "traffic": traffic,
                      "algorithmic_bytes_per_launch": algo_bytes,
-                     "algorithmic_hbm_gbs": round(algo_bytes / (ms * 1e-3) / 1e9, 1)},
+                     "algorithmic_hbm_gbs": round(algo_bytes / (ms * 1e-3) / 1e9, 1),
+                     "secondary_ceilings": secondary_ceilings(d, dtype, causal, fl, _lib.fwd_tile(
+                         N, d, causal, {"f16": 0, "bf16": 1, "fp8": 2}[dtype]), rec)},
+        "configs": configs,
         "sweep": sweep,
-        "timing": "HIP events on the kernel's stream; value = K back-to-back calls / elapsed; per_call and "
-                  "sweep = one event pair per call (median, min, p90); no cache flush between calls",
+        "timing": "HIP events on the kernel's stream; value = K back-to-back calls / elapsed after "
+                  f"{args.clock_ms:g} ms of clock conditioning (device matmuls, not the benchmarked call) and W "
+                  "warm-up calls; per_call, configs and sweep = one event pair per call (median, min, p90), each "
+                  "after a 50 ms warm-up; no cache flush between calls",
         "gpu_clocks_under_load": clocks,
     }
     if not args.no_cpu:

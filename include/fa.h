@@ -204,6 +204,29 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
 int fa_qkv_proj(const void* x, const void* w, const void* bias, void* q, void* k, void* v,
                 int B, int N, int D, int H, int d, int dtype, void* stream);
 
+/*
+ * fa_fwd_tile -- which compiled kernel shape a forward call with these
+ * arguments runs (a query about this library, not an operation of the
+ * pages).  The shape is chosen from N, d, the mask and the dtype, and the
+ * FA_TILE environment variable (QWxNWxBCxSCHEDxWPE) may select another
+ * compiled shape; this reports the outcome, so a caller can tell whether an
+ * FA_TILE request was honoured or fell back to the default.
+ *
+ *   N       sequence length (fa_fwd_varlen: max_seqlen), >= 1.
+ *   d       64 or 128.   causal, dtype  as for fa_fwd.
+ *   mode    FA_TILE_DENSE (fa_fwd, fa_fwd_fp8), FA_TILE_VARLEN (fa_fwd_varlen)
+ *           or FA_TILE_DROPOUT (fa_fwd_dropout; FA_TILE is ignored there).
+ *   tile    out, 5 ints: query rows per wave, waves per workgroup, keys per
+ *           tile, schedule (0 = every wave runs each tile's products and
+ *           softmax in turn, 1 = two wave groups alternate them), and the
+ *           waves per SIMD the kernel's registers are budgeted for.
+ * Returns FA_OK, FA_ERR_NULL_PTR, FA_ERR_SHAPE (N < 1 or an unknown mode),
+ * FA_ERR_HEADDIM or FA_ERR_DTYPE (unknown, or fp8 with FA_TILE_DROPOUT).
+ * Makes no HIP call.
+ */
+enum { FA_TILE_DENSE = 0, FA_TILE_VARLEN = 1, FA_TILE_DROPOUT = 2 };
+int fa_fwd_tile(int N, int d, int causal, int dtype, int mode, int* tile);
+
 /* Static description of a return code; never NULL. */
 const char* fa_strerror(int code);
 

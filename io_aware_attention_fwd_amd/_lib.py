@@ -1,7 +1,7 @@
 """ctypes binding of libfa.so: argument marshalling only.
 
 ``fa_fwd``, ``fa_fwd_fp8``, ``fa_fwd_varlen``, ``fa_fwd_dropout``, ``fa_bwd``,
-``fa_qkv_proj``, ``fa_strerror`` and ``fa_version`` take the same arguments as
+``fa_qkv_proj``, ``fa_fwd_tile``, ``fa_strerror`` and ``fa_version`` take the same arguments as
 the C functions declared in ``include/fa.h`` (device pointers as Python ints,
 the stream as a ``hipStream_t`` int or None).  ``fwd``, ``fwd_varlen``,
 ``fwd_dropout``, ``bwd`` and ``qkv_proj`` allocate
@@ -34,7 +34,9 @@ class FaError(RuntimeError):
 
 
 def library_path() -> str:
-    return os.path.join(_HERE, "libfa.so")
+    """The in-tree libfa.so, or the build named by the FA_LIBRARY environment
+    variable (used to run the CPU ABI tests against an instrumented host build)."""
+    return os.environ.get("FA_LIBRARY") or os.path.join(_HERE, "libfa.so")
 
 
 def load() -> ctypes.CDLL:
@@ -60,6 +62,8 @@ def load() -> ctypes.CDLL:
     lib.fa_bwd.restype = ci
     lib.fa_qkv_proj.argtypes = [vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, vp]
     lib.fa_qkv_proj.restype = ci
+    lib.fa_fwd_tile.argtypes = [ci, ci, ci, ci, ci, ctypes.POINTER(ctypes.c_int)]
+    lib.fa_fwd_tile.restype = ci
     lib.fa_strerror.argtypes = [ci]
     lib.fa_strerror.restype = ctypes.c_char_p
     lib.fa_version.argtypes = []
@@ -93,6 +97,24 @@ def fa_qkv_proj(x, w, bias, q, k, v, B, N, D, H, d, dtype, stream) -> int:
     return load().fa_qkv_proj(x, w, bias, q, k, v, B, N, D, H, d, dtype, stream)
 
 
+FA_TILE_DENSE = 0
+FA_TILE_VARLEN = 1
+FA_TILE_DROPOUT = 2
+
+
+def fa_fwd_tile(N, d, causal, dtype, mode, tile) -> int:
+    return load().fa_fwd_tile(N, d, int(causal), dtype, mode, tile)
+
+
+def fwd_tile(N: int, d: int, causal: bool, dtype: int, mode: int = FA_TILE_DENSE) -> str:
+    """The kernel shape a forward call runs, as the FA_TILE string QWxNWxBCxSCHEDxWPE."""
+    t = (ctypes.c_int * 5)()
+    rc = fa_fwd_tile(N, d, causal, dtype, mode, t)
+    if rc != 0:
+        raise FaError(rc, "fa_fwd_tile")
+    return "x".join(str(x) for x in t)
+
+
 def fa_strerror(code: int) -> str:
     return load().fa_strerror(code).decode()
 
@@ -102,6 +124,34 @@ def fa_version() -> int:
 
 
 _TORCH_DTYPES = {torch.float16: FA_DTYPE_F16, torch.bfloat16: FA_DTYPE_BF16, torch.float8_e4m3fn: FA_DTYPE_FP8_E4M3}
+
+
+def _require(t: torch.Tensor, name: str, shape=None, dtype=None) -> None:
+    """Shape, dtype and contiguity of one tensor argument (before any device check)."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _same_device(ref: torch.Tensor, stream, **tensors) -> None:
+    """Every tensor (and the stream, if given) on the GPU that holds ``ref``.
+
+    Runs after the shape checks and before the library call: the kernels take
+    raw device pointers, so a host tensor or one on another GPU would make
+    them read or write memory that is not the tensor's.
+    """
+    if ref.device.type != "cuda":
+        raise ValueError(f"tensors must be on a GPU, got {ref.device}")
+    for name, t in tensors.items():
+        if t is not None and t.device != ref.device:
+            raise ValueError(f"{name} is on {t.device}, not on {ref.device} with the other inputs")
+    if stream is not None and getattr(stream, "device", ref.device) != ref.device:
+        raise ValueError(f"stream belongs to {stream.device}, not to {ref.device}")
 
 
 def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: float, causal: bool = False, *,
@@ -123,12 +173,15 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: float, causal:
     B, H, N, d = q.shape
     dt = _TORCH_DTYPES[q.dtype]
     o_dtype = torch.bfloat16 if dt == FA_DTYPE_FP8_E4M3 else q.dtype
+    if out is not None:
+        _require(out, "out", (B, H, N, d), o_dtype)
+    if lse is not None:
+        _require(lse, "lse", (B, H, N), torch.float32)
+    _same_device(q, stream, k=k, v=v, out=out, lse=lse)
     if out is None:
         out = torch.empty((B, H, N, d), dtype=o_dtype, device=q.device)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    if out.dtype != o_dtype or lse.dtype != torch.float32:
-        raise TypeError("out/lse dtype mismatch")
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     s = stream.cuda_stream
@@ -155,6 +208,7 @@ def fwd_dropout(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: float,
     if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
         raise ValueError("q, k, v must be contiguous")
     B, H, N, d = q.shape
+    _same_device(q, stream, k=k, v=v)
     out = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     if stream is None:
@@ -189,12 +243,15 @@ def fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: to
     B = cu_seqlens.numel() - 1
     dt = _TORCH_DTYPES[q.dtype]
     o_dtype = torch.bfloat16 if dt == FA_DTYPE_FP8_E4M3 else q.dtype
+    if out is not None:
+        _require(out, "out", (total, H, d), o_dtype)
+    if lse is not None:
+        _require(lse, "lse", (H, total), torch.float32)
+    _same_device(q, stream, k=k, v=v, cu_seqlens=cu_seqlens, out=out, lse=lse)
     if out is None:
         out = torch.empty((total, H, d), dtype=o_dtype, device=q.device)
     if lse is None:
         lse = torch.empty((H, total), dtype=torch.float32, device=q.device)
-    if out.dtype != o_dtype or lse.dtype != torch.float32:
-        raise TypeError("out/lse dtype mismatch")
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     rc = fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), cu_seqlens.data_ptr(),
@@ -217,6 +274,7 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse:
     B, H, N, d = q.shape
     if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N) or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+    _same_device(q, stream, k=k, v=v, o=o, lse=lse, dout=dout)
     dq, dk, dv = (torch.empty_like(q) for _ in range(3))
     delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     if stream is None:
@@ -240,6 +298,7 @@ def qkv_proj(x: torch.Tensor, w: torch.Tensor, bias: torch.Tensor | None, H: int
     if not (x.is_contiguous() and w.is_contiguous() and (bias is None or bias.is_contiguous())):
         raise ValueError("x, w and bias must be contiguous")
     B, N, D = x.shape
+    _same_device(x, stream, w=w, bias=bias)
     q, k, v = (torch.empty((B, H, N, d), dtype=x.dtype, device=x.device) for _ in range(3))
     if stream is None:
         stream = torch.cuda.current_stream(x.device)

@@ -6,10 +6,12 @@
 #include "fa.h"
 
 #include <hip/hip_runtime.h>
+#include <float.h>
 #include <math.h>
 #include <stdint.h>
 
 #include "fa_launch.h"
+#include "fa_variants.h"
 
 namespace {
 
@@ -49,7 +51,8 @@ int forward(const void* q, const void* k, const void* v, void* o, float* lse, co
   if (!isfinite(scale) || !isfinite(q_descale) || !isfinite(k_descale) || !isfinite(v_descale)) return FA_ERR_SCALE;
   const int eb = elem_bytes(dt);
   const int ob = 2;  // O is binary16 / bfloat16 (bfloat16 for fp8 inputs)
-  const int br = fa::rows_per_workgroup(dt, d, causal != 0, L.N, drop.t < 256, packed);
+  const int vi = fa::selected_variant(dt, d, causal != 0, L.N, drop.t < 256, packed);
+  const int br = fa::kVariants[vi].qw * fa::kVariants[vi].nw;  // query rows per workgroup
   // The rows of one (sequence, head), plus the padding rows of its last tile,
   // must be addressable with 32-bit byte offsets (the kernels use buffer loads).
   const int64_t in_row = packed ? (int64_t)L.H * d * eb : (int64_t)d * eb;
@@ -107,13 +110,15 @@ int forward(const void* q, const void* k, const void* v, void* o, float* lse, co
   const uint32_t sign_bits = dt == fa::Dtype::FP8 ? 0x80808080u : 0x80008000u;
   p.q_xor = eff < 0 ? sign_bits : 0u;
   p.q_and = eff == 0 ? 0u : 0xFFFFFFFFu;
-  p.c = eff == 0 ? 1.0f : (float)(fabs(eff) * (double)kLog2e);
-  if (!isfinite(p.c)) return FA_ERR_SCALE;
+  const double c = eff == 0 ? 1.0 : fabs(eff) * (double)kLog2e;
+  if (!(c <= (double)FLT_MAX)) return FA_ERR_SCALE;  // checked in double: a float conversion out of range is undefined
+  p.c = (float)c;
   p.o_mul = v_descale * (float)(256.0 / drop.t);
   p.drop_t = drop.t;
   p.seed_lo = (uint32_t)drop.seed;
   p.seed_hi = (uint32_t)(drop.seed >> 32);
   p.drop_offset = drop.offset;
+  p.variant = vi;
 
   if (packed && L.total == 0) return FA_OK;  // no rows: nothing to compute
   if (fa::launch_fwd(dt, d, causal != 0, p, static_cast<hipStream_t>(stream)) != hipSuccess) return FA_ERR_HIP;
@@ -148,6 +153,8 @@ int backward(const void* q, const void* k, const void* v, const void* o, const f
     for (int j = i + 1; j < 4; ++j)
       if (overlap(outs[i], out_sz[i], outs[j], out_sz[j])) return FA_ERR_ALIAS;
   }
+  const double c = (double)scale * (double)kLog2e;
+  if (!(fabs(c) <= (double)FLT_MAX)) return FA_ERR_SCALE;  // checked in double, before the float conversion
   fa::BwdParams p;
   p.q = q;
   p.k = k;
@@ -164,9 +171,8 @@ int backward(const void* q, const void* k, const void* v, const void* o, const f
   p.N = N;
   p.n_blocks = (int)n_blocks;
   p.total_wg = (int)total_wg;
-  p.c = (float)((double)scale * (double)kLog2e);
+  p.c = (float)c;
   p.scale = scale;
-  if (!isfinite(p.c)) return FA_ERR_SCALE;
   if (fa::launch_bwd(static_cast<fa::Dtype>(dtype), d, causal != 0, p, static_cast<hipStream_t>(stream)) != hipSuccess)
     return FA_ERR_HIP;
   return FA_OK;
@@ -278,6 +284,23 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
 int fa_qkv_proj(const void* x, const void* w, const void* bias, void* q, void* k, void* v, int B, int N, int D, int H,
                 int d, int dtype, void* stream) {
   return qkv_proj(x, w, bias, q, k, v, B, N, D, H, d, dtype, stream);
+}
+
+int fa_fwd_tile(int N, int d, int causal, int dtype, int mode, int* tile) {
+  if (!tile) return FA_ERR_NULL_PTR;
+  if (!known_dtype(dtype)) return FA_ERR_DTYPE;
+  if (mode != FA_TILE_DENSE && mode != FA_TILE_VARLEN && mode != FA_TILE_DROPOUT) return FA_ERR_SHAPE;
+  if (mode == FA_TILE_DROPOUT && dtype == FA_DTYPE_FP8_E4M3) return FA_ERR_DTYPE;
+  if (N < 1) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+  const fa::Variant& v = fa::kVariants[fa::selected_variant(static_cast<fa::Dtype>(dtype), d, causal != 0, N,
+                                                            mode == FA_TILE_DROPOUT, mode == FA_TILE_VARLEN)];
+  tile[0] = v.qw;
+  tile[1] = v.nw;
+  tile[2] = v.bc;
+  tile[3] = v.sched;
+  tile[4] = v.wpe;
+  return FA_OK;
 }
 
 const char* fa_strerror(int code) {

@@ -38,6 +38,7 @@ struct FwdParams {
   // key (seed_lo, seed_hi); counter word 3 is drop_offset.
   uint32_t drop_t;
   uint32_t seed_lo, seed_hi, drop_offset;
+  int variant;    // index into kVariants (fa_variants.h) of the tile shape to run
 };
 
 // Backward pass over dense [B,H,N,d] tensors (16-bit types).
@@ -80,10 +81,6 @@ struct ProjTiling {
 ProjTiling proj_tiling(int64_t M, int64_t ncol);
 
 enum class Dtype { F16 = 0, BF16 = 1, FP8 = 2 };
-
-// Rows of Q one workgroup owns for the instance chosen for this call (sizes the
-// grid).  packed: sequences of different lengths (cu_seqlens), N their maximum.
-int rows_per_workgroup(Dtype dt, int d, bool causal, int N, bool dropout, bool packed);
 
 // Enqueue one forward pass; returns hipSuccess or the launch error.
 hipError_t launch_fwd(Dtype dt, int d, bool causal, const FwdParams& p, hipStream_t stream);

@@ -161,6 +161,32 @@ def structured(B: int, H: int, N: int, d: int, dtype: str, period: int = 64) -> 
     return store(dtype, q32, k32, v32)
 
 
+def onehot_blocks(B: int, H: int, N: int, d: int, dtype: str, block: int = 8) -> Inputs:
+    """Full-size inputs whose exact output is known for every row of every slice.
+
+    Q = 0 (every score is 0 whatever K holds, so each query averages the
+    values of the keys it may see), K = small integers in [-3, 3] (seed 2),
+    and V one-hot by key block: V[b, h, j, c] = 1 if (j // block + b*H + h)
+    mod d == c, else 0.  Every value is exact in every storage format (fp8
+    with descale 1).  A dropped, duplicated or misplaced block of ``block``
+    keys moves the visible-key count of one column, and a slice read in
+    place of another shifts the columns.
+    """
+    rng = np.random.default_rng(2)
+    k32 = rng.integers(-3, 4, size=(B, H, N, d), dtype=np.int8).astype(np.float32)
+    q32 = np.zeros((B, H, N, d), np.float32)
+    col = (np.arange(N)[None, None, :] // block + np.arange(B * H).reshape(B, H, 1)) % d  # [B, H, N]
+    v32 = (col[..., None] == np.arange(d)).astype(np.float32)
+    if dtype == "fp8":
+        # E4M3 codes: 0 -> 0x00, 1 -> 0x38; the small integers of K through the encoder
+        import torch
+
+        enc = lambda a: torch.from_numpy(a).to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
+        return Inputs("fp8", np.zeros(q32.shape, np.uint8), enc(k32), np.where(v32 > 0, 0x38, 0).astype(np.uint8),
+                      {"q": 1.0, "k": 1.0, "v": 1.0})
+    return store(dtype, q32, k32, v32)
+
+
 @dataclass
 class ProjectionInputs:
     """Stored inputs of one QKV projection: x [B, N, D], w [3 H d, D] and

@@ -9,12 +9,13 @@ Runs ``bench.py`` under ``rocprofv3`` (each run a child process started from
   with its default warm-up and step counts (the same command bench.py's line
   comes from), the forward kernel's average duration and the TFLOP/s it
   implies;
-* for the headline workload only (no ``--shape``): ``<tag>_counters.md`` and
-  ``<tag>_traffic.json`` from three counter runs, ``--pmc FETCH_SIZE`` and
-  ``--pmc WRITE_SIZE`` (one counter per run, each next to a 256 MiB device
-  copy whose known size calibrates the counter) and one run of SQ counters.
-  The JSON carries the hash of the kernel sources it was taken on; bench.py
-  reports the traffic only while that hash matches the sources.
+* unless ``--no-counters``: ``<tag>_counters.md`` and ``<tag>_traffic.json``
+  from four counter runs, ``--pmc FETCH_SIZE`` and ``--pmc WRITE_SIZE`` (one
+  counter per run, each next to a 256 MiB device copy whose known size
+  calibrates the counter), one run of SQ counters and one of instruction
+  counts.  The JSON carries the hash of the kernel sources it was taken on;
+  bench.py reports its traffic and instruction-based ceiling only while that
+  hash matches the sources.
 
 ``tag`` names the kernel and workload, e.g. ``fa_fwd_f16_b8h32n1024d64``.
 
@@ -47,6 +48,11 @@ COPY_MIB = 256
 HEADLINE = (8, 32, 1024, 64, "f16", False)
 SQ_COUNTERS = ["SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CU_CYCLES",
                "SQ_ACTIVE_INST_VALU", "SQ_WAVE_CYCLES", "SQ_WAIT_INST_LDS", "GRBM_GUI_ACTIVE"]
+# instruction counts (per wave, summed over the dispatch) behind the vector-ALU ceiling bench.py reports:
+# all vector ALU instructions (matrix ones included), the transcendental ones, the matrix ones, LDS ones
+INSTR_COUNTERS = {"valu": "SQ_INSTS_VALU", "valu_trans": "SQ_INSTS_VALU_TRANS_F32", "mfma": "SQ_INSTS_MFMA",
+                  "lds": "SQ_INSTS_LDS"}
+MODE_FAMILY = {"varlen": "fwd", "dropout": "fwd", "bwd": "bwd", "proj": "proj"}
 
 
 def _bench_args(shape, steps=None, warmup=None, extra=()):
@@ -64,11 +70,27 @@ def _profile(prof_args, bench_args, out_dir, tag, timeout=300):
                                         sys.executable, os.path.join(ROOT, "bench.py")] + bench_args)
     proc = subprocess.run(cmd, cwd="/tmp", env=dict(os.environ, TMPDIR="/tmp"), timeout=timeout,
                           stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
-    # rocprofv3 may end with SIGSEGV after a complete run; the CSVs decide
-    if proc.returncode not in (0, -11, 139):
+    # rocprofv3 can end with SIGSEGV after the profiled program has finished
+    # and its CSVs are complete: the run is used (the caller still needs its
+    # CSVs) but the exit status is kept and written into the summary
+    if proc.returncode in (-11, 139):
+        PROFILER_CRASHES.append((" ".join(prof_args), proc.returncode))
+    elif proc.returncode != 0:
         raise RuntimeError(f"{' '.join(cmd)} failed ({proc.returncode}):\n{proc.stdout[-2000:]}")
     lines = [l for l in proc.stdout.splitlines() if l.startswith("{")]
     return " ".join(prof_args), (json.loads(lines[-1]) if lines else None)
+
+
+# (profiler arguments, exit status) of every profiler run of this process that ended with SIGSEGV
+PROFILER_CRASHES = []
+
+
+def _crash_note():
+    if not PROFILER_CRASHES:
+        return "Profiler exit status: 0 for every run.\n"
+    runs = "; ".join(f"`{a}` exited {rc}" for a, rc in PROFILER_CRASHES)
+    return (f"Profiler exit status: {runs} (SIGSEGV of rocprofv3 after the program finished; the CSVs it "
+            f"had written were complete and are the ones used).\n")
 
 
 def _counter_means(out_dir):
@@ -91,7 +113,7 @@ def tag_of(shape):
     return f"fa_fwd_{dt}_b{B}h{H}n{N}d{d}" + ("_causal" if causal else "")
 
 
-def record(shape, out_dir):
+def record(shape, out_dir, counters=True):
     os.makedirs(out_dir, exist_ok=True)
     B, H, N, d, dt, causal = shape
     tag = tag_of(shape)
@@ -117,7 +139,8 @@ def record(shape, out_dir):
                 f.write(f"  The same command's bench.py line (HIP events over the timed region, profiler attached) "
                         f"reported {line['ms_per_step'] * 1e3:.1f} us per step, {line['value']:.1f} TFLOP/s.")
             f.write(f"\n\nKernel source hash (bench.kernel_source_hash): {bench.kernel_source_hash()}\n")
-        if shape != HEADLINE:
+            f.write(_crash_note())
+        if not counters:
             return
 
         raw, factor, cmds = {}, {}, []
@@ -133,12 +156,16 @@ def record(shape, out_dir):
         pargs, _ = _profile(["--pmc"] + SQ_COUNTERS, bargs, os.path.join(wd, "sq"), "sq")
         sq_cmd = _display(pargs, bargs)
         sq = {k[2]: v for k, v in _counter_means(os.path.join(wd, "sq")).items() if k[0]}
+        pargs, _ = _profile(["--pmc"] + list(INSTR_COUNTERS.values()), bargs, os.path.join(wd, "insts"), "insts")
+        inst_cmd = _display(pargs, bargs)
+        ic = {k[2]: v for k, v in _counter_means(os.path.join(wd, "insts")).items() if k[0]}
+        instructions = {key: ic.get(name) for key, name in INSTR_COUNTERS.items()}
 
     fetch = round(raw["FETCH_SIZE"] * 1024 * factor["FETCH_SIZE"])
     write = round(raw["WRITE_SIZE"] * 1024 * factor["WRITE_SIZE"])
     traffic = {
         "kernel": row["Name"], "workload": f"attention forward {desc}",
-        "kernel_source_sha256_16": bench.kernel_source_hash(),
+        "kernel_source_sha256_16": bench.kernel_source_hash("fwd"),
         "fetch_size_kib_per_dispatch_raw": raw["FETCH_SIZE"], "write_size_kib_per_dispatch_raw": raw["WRITE_SIZE"],
         "calibration": {"reference_kernel": f"__amd_rocclr_copyBuffer (device copy of {COPY_MIB} MiB)",
                         "expected_kib_each_way": COPY_MIB * 1024,
@@ -147,6 +174,7 @@ def record(shape, out_dir):
         "fetch_bytes_per_launch": fetch, "write_bytes_per_launch": write, "bytes_per_launch": fetch + write,
         "algorithmic_bytes_per_launch": algo, "ratio_to_algorithmic": round((fetch + write) / algo, 4),
         "commands": cmds,
+        "instructions": instructions, "instruction_counters": INSTR_COUNTERS, "instruction_command": inst_cmd,
     }
     with open(os.path.join(out_dir, f"{tag}_traffic.json"), "w") as f:
         json.dump(traffic, f, indent=1)
@@ -170,8 +198,14 @@ def record(shape, out_dir):
         f.write(f"## SQ counters (one run)\n\n```\n{sq_cmd}\n```\n\n| counter | mean per dispatch |\n|---|---|\n")
         for k in sorted(sq):
             f.write(f"| {k} | {sq[k]:.0f} |\n")
+        f.write(f"\n## Instruction counts (one run; per-wave instructions summed over the dispatch)\n\n"
+                f"```\n{inst_cmd}\n```\n\n| counter | mean per dispatch |\n|---|---|\n")
+        for k, name in INSTR_COUNTERS.items():
+            v = instructions.get(k)
+            f.write(f"| {name} | {'n/a' if v is None else f'{v:.0f}'} |\n")
         f.write(f"\nGRBM_GUI_ACTIVE is summed over the 8 XCDs ({grbm / 8:.0f} cycles each); MFMA busy / "
                 f"(cycles x 1024 SIMDs) = {100 * mfma / (grbm / 8 * 1024):.1f}% under the counter run.\n")
+        f.write(_crash_note())
 
 
 def record_mode(mode, mode_arg, tag, out_dir):
@@ -199,7 +233,9 @@ def record_mode(mode, mode_arg, tag, out_dir):
                     f"{flop / per_step_ns / 1e3:.1f} TFLOP/s at bench.py's {flop / 1e9:.1f} GFLOP per step.  The same "
                     f"command's bench.py line (HIP events over the timed region, profiler attached) reported "
                     f"{line['ms_per_step'] * 1e3:.1f} us per step, {line['value']:.1f} TFLOP/s.\n")
-        f.write(f"\nKernel source hash (bench.kernel_source_hash): {bench.kernel_source_hash()}\n")
+        fam = MODE_FAMILY[mode]
+        f.write(f"\nKernel source hash (bench.kernel_source_hash(\"{fam}\")): {bench.kernel_source_hash(fam)}\n")
+        f.write(_crash_note())
 
 
 def main(argv=None):
@@ -209,6 +245,8 @@ def main(argv=None):
     ap.add_argument("--mode", default=None, choices=["varlen", "dropout", "bwd", "proj"])
     ap.add_argument("--mode-arg", default=None, help="the argument bench.py takes for --MODE")
     ap.add_argument("--tag", default=None, help="file name stem for --mode")
+    ap.add_argument("--no-counters", action="store_true",
+                    help="kernel statistics only (no FETCH_SIZE / WRITE_SIZE / SQ / instruction counter runs)")
     args = ap.parse_args(argv)
     if args.mode:
         record_mode(args.mode, args.mode_arg, args.tag, args.out_dir)
@@ -218,7 +256,7 @@ def main(argv=None):
     if args.shape:
         B, H, N, d, dt, causal = args.shape.split(",")
         shape = (int(B), int(H), int(N), int(d), dt, causal in ("1", "true"))
-    record(shape, args.out_dir)
+    record(shape, args.out_dir, counters=not args.no_counters)
     print(f"recorded {tag_of(shape)} into {args.out_dir}", flush=True)
     return 0
 

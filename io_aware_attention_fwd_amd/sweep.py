@@ -39,11 +39,23 @@ DEFAULT_WORKLOADS = ["8,32,1024,64,f16,0", "8,32,8192,64,f16,0", "8,32,4096,64,b
 COPY_MIB = 256
 
 
+VARIANTS_H = os.path.join(HERE, "csrc", "fa_variants.h")
+
+
 def variants():
-    """FA_TILE strings of the compiled variants, read from the kernel source."""
-    src = open(os.path.join(HERE, "csrc", "fa_fwd.hip")).read()
-    body = re.search(r"constexpr Variant kVariants\[\] = \{(.*?)\};", src, re.S).group(1)
+    """FA_TILE strings of the compiled variants, read from the variant table."""
+    src = open(VARIANTS_H).read()
+    body = re.search(r"kVariants\[\] = \{(.*?)\};", src, re.S).group(1)
     return ["x".join(t.split(",")).replace(" ", "") for t in re.findall(r"\{([\d,\s]+)\}", body)]
+
+
+def variants_per_d():
+    """(d, FA_TILE) of every shape compiled for head dimension d."""
+    src = open(VARIANTS_H).read()
+    only = {n: {int(i) for i in re.findall(r"v == (\d+)", re.search(n + r"\(int v\) \{(.*?)\}", src).group(1))}
+            for n in ("d64_only", "d128_only")}
+    return [(d, t) for d in (64, 128) for i, t in enumerate(variants())
+            if not (i in only["d64_only"] and d != 64) and not (i in only["d128_only"] and d != 128)]
 
 
 def _rocprof(args, out_dir, tag, env, timeout):
@@ -52,13 +64,27 @@ def _rocprof(args, out_dir, tag, env, timeout):
     return cmd
 
 
-def _run(cmd, env, timeout):
+def _run(cmd, env, timeout, crashes):
+    """Run one profiler command.  rocprofv3 can end with SIGSEGV (-11 / 139)
+    after the profiled program has finished and its CSVs are complete; such a
+    run is kept (the caller still needs its CSVs, or raises without them) but
+    its exit status is appended to ``crashes``, so the row it feeds says so."""
     proc = subprocess.run(cmd, cwd="/tmp", env=env, timeout=timeout, stdout=subprocess.PIPE,
                           stderr=subprocess.STDOUT, text=True)
-    # rocprofv3 may end with SIGSEGV after a complete run; the CSVs decide
-    if proc.returncode not in (0, -11, 139):
+    if proc.returncode in (-11, 139):
+        crashes.append(proc.returncode)
+    elif proc.returncode != 0:
         raise RuntimeError(f"{' '.join(cmd)} failed ({proc.returncode}):\n{proc.stdout[-2000:]}")
     return proc.stdout
+
+
+KERNEL_RE = re.compile(r"fa_fwd_kernel<[^,]+, (\d+), (?:true|false), (\d+), (\d+), (\d+), (\d+), (\d+)")
+
+
+def tile_of_kernel(name):
+    """The FA_TILE string (QWxNWxBCxSCHEDxWPE) of a forward kernel instance name, or None."""
+    m = KERNEL_RE.search(name)
+    return "x".join(m.groups()[1:]) if m else None
 
 
 def _counters(path, kernel_substr="fa_fwd_kernel"):
@@ -81,21 +107,26 @@ def measure(tile, workload, workdir, timeout=300):
     env = dict(os.environ, FA_TILE=tile, TMPDIR="/tmp")
     shape = ["--shape", workload]
     res = {"tile": tile, "workload": workload}
+    crashes = []
     # 1. duration
     out = os.path.join(workdir, "trace")
     # bench.py's default warm-up and steps, so the clock has left its idle level
-    _run(_rocprof(["--kernel-trace", "--stats"], out, "t", env, timeout) + shape, env, timeout)
+    _run(_rocprof(["--kernel-trace", "--stats"], out, "t", env, timeout) + shape, env, timeout, crashes)
     rows = [r for f in glob.glob(os.path.join(out, "*_kernel_stats.csv")) for r in csv.DictReader(open(f))
             if "fa_fwd_kernel" in r["Name"]]
+    if not rows:
+        raise RuntimeError(f"no forward kernel in the kernel trace of {workload} with FA_TILE={tile}")
     avg_ns = float(rows[0]["AverageNs"])
     flop = 4.0 * B * H * N * N * d / (2 if causal else 1)
     res["kernel"] = rows[0]["Name"]
+    # the instance that ran, from its name: a request the library did not honour shows here
+    res["tile_ran"] = tile_of_kernel(rows[0]["Name"])
     res["avg_us"] = round(avg_ns / 1e3, 2)
     res["tflops"] = round(flop / avg_ns / 1e3, 1)
     # 2. SQ counters
     out = os.path.join(workdir, "sq")
     _run(_rocprof(["--pmc", "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE"],
-                  out, "s", env, timeout) + shape + ["--steps", "2", "--warmup", "1"], env, timeout)
+                  out, "s", env, timeout) + shape + ["--steps", "2", "--warmup", "1"], env, timeout, crashes)
     c = _counters(out)
     mfma = _mean(c.get((True, False, "SQ_VALU_MFMA_BUSY_CYCLES"), []))
     grbm = _mean(c.get((True, False, "GRBM_GUI_ACTIVE"), []))  # summed over the 8 XCDs
@@ -107,13 +138,14 @@ def measure(tile, workload, workdir, timeout=300):
     for counter in ("FETCH_SIZE", "WRITE_SIZE"):
         out = os.path.join(workdir, counter.lower())
         _run(_rocprof(["--pmc", counter], out, counter.lower(), env, timeout) + shape +
-             ["--steps", "2", "--warmup", "1", "--copy-calib-mib", str(COPY_MIB)], env, timeout)
+             ["--steps", "2", "--warmup", "1", "--copy-calib-mib", str(COPY_MIB)], env, timeout, crashes)
         c = _counters(out)
         copy = _mean(c.get((False, True, counter), []))
         factor = COPY_MIB * 1024 / copy if copy > 0 else float("nan")
         traffic[counter] = _mean(c.get((True, False, counter), [])) * 1024 * factor
     res["hbm_bytes"] = round(traffic["FETCH_SIZE"] + traffic["WRITE_SIZE"])
     res["hbm_gbs"] = round(res["hbm_bytes"] / (avg_ns * 1e-9) / 1e9, 1)
+    res["profiler_crashes"] = crashes  # exit statuses of profiler runs that ended with SIGSEGV
     return res
 
 
@@ -124,27 +156,29 @@ def main(argv=None):
     ap.add_argument("--out", default=None, help="write a markdown table here")
     args = ap.parse_args(argv)
     tiles = args.tiles or variants()
+    compiled = set(variants_per_d())
     results = []
     for w in args.workloads:
         for t in tiles:
             d = int(w.split(",")[3])
-            if t in ("64x8x64x1x2", "32x16x64x1x4", "32x8x64x0x4") and d != 64:
-                continue  # shapes compiled for d = 64 only
-            if t == "64x8x32x1x2" and d != 128:
-                continue  # compiled for d = 128 only
+            if (d, t) not in compiled:
+                continue  # not compiled for this head dimension
             with tempfile.TemporaryDirectory(dir="/tmp") as wd:
                 r = measure(t, w, wd)
             print(json.dumps(r), flush=True)
             results.append(r)
     if args.out:
         with open(args.out, "w") as f:
-            f.write("| workload (B,H,N,d,dtype,causal) | FA_TILE (QW x NW x BC x schedule x waves/SIMD) | us | TFLOP/s "
-                    "| MFMA busy | LDS bank-conflict cycles | LDS active cycles | HBM bytes | HBM GB/s |\n")
-            f.write("|---|---|---|---|---|---|---|---|---|\n")
+            f.write("| workload (B,H,N,d,dtype,causal) | FA_TILE (QW x NW x BC x schedule x waves/SIMD) | instance "
+                    "that ran | us | TFLOP/s | MFMA busy | LDS bank-conflict cycles | LDS active cycles | HBM bytes "
+                    "| HBM GB/s | profiler SIGSEGV |\n")
+            f.write("|---|---|---|---|---|---|---|---|---|---|---|\n")
             for r in results:
-                f.write(f"| {r['workload']} | {r['tile']} | {r['avg_us']} | {r['tflops']} | {r['mfma_util']} | "
+                ran = r["tile_ran"] if r["tile_ran"] == r["tile"] else f"**{r['tile_ran']}** (not the request)"
+                crash = ", ".join(str(c) for c in r["profiler_crashes"]) or "none"
+                f.write(f"| {r['workload']} | {r['tile']} | {ran} | {r['avg_us']} | {r['tflops']} | {r['mfma_util']} | "
                         f"{r['lds_bank_conflict_cycles']:.0f} | {r['lds_active_cycles']:.0f} | {r['hbm_bytes']} | "
-                        f"{r['hbm_gbs']} |\n")
+                        f"{r['hbm_gbs']} | {crash} |\n")
     return 0
 
 

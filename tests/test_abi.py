@@ -40,8 +40,8 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     declared = _declared_functions()
-    assert declared == ["fa_bwd", "fa_fwd", "fa_fwd_dropout", "fa_fwd_fp8", "fa_fwd_varlen", "fa_qkv_proj",
-                        "fa_strerror", "fa_version"]
+    assert declared == ["fa_bwd", "fa_fwd", "fa_fwd_dropout", "fa_fwd_fp8", "fa_fwd_tile",
+                        "fa_fwd_varlen", "fa_qkv_proj", "fa_strerror", "fa_version"]
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.library_path()], capture_output=True, text=True, check=True).stdout
     exported = set(re.findall(r"\bT (fa_\w+)$", out, flags=re.M))
     for name in declared:
@@ -257,3 +257,90 @@ def test_python_wrapper_rejects_mismatched_shapes():
         _lib.fwd_varlen(q[0], q[0], q[0], torch.zeros(3, dtype=torch.int64), 8, 0.1)
     with pytest.raises(ValueError):
         _lib.fwd_varlen(q, q, q, torch.zeros(3, dtype=torch.int32), 8, 0.1)
+
+
+# ---- fa_fwd_tile: the kernel shape a call runs (host logic, no HIP call)
+def _tile(N, d, causal, dtype, mode=_lib.FA_TILE_DENSE):
+    return _lib.fwd_tile(N, d, causal, dtype, mode)
+
+
+def _compiled_tiles():
+    """(FA_TILE string, d64 only, d128 only) of every compiled shape, read from the variant table."""
+    src = open(os.path.join(ROOT, "io_aware_attention_fwd_amd", "csrc", "fa_variants.h")).read()
+    body = re.search(r"kVariants\[\] = \{(.*?)\};", src, re.S).group(1)
+    tiles = ["x".join(t.replace(" ", "").split(",")) for t in re.findall(r"\{([\d,\s]+)\}", body)]
+    d64 = {int(i) for i in re.findall(r"v == (\d+)", re.search(r"d64_only\(int v\) \{(.*?)\}", src).group(1))}
+    d128 = {int(i) for i in re.findall(r"v == (\d+)", re.search(r"d128_only\(int v\) \{(.*?)\}", src).group(1))}
+    return [(t, i in d64, i in d128) for i, t in enumerate(tiles)]
+
+
+def test_tile_query_rejects(lib):
+    t = (ctypes.c_int * 5)()
+    codes = _codes()
+    assert _lib.fa_fwd_tile(100, 64, 0, 0, 0, None) == codes["FA_ERR_NULL_PTR"]
+    assert _lib.fa_fwd_tile(0, 64, 0, 0, 0, t) == codes["FA_ERR_SHAPE"]
+    assert _lib.fa_fwd_tile(100, 64, 0, 0, 7, t) == codes["FA_ERR_SHAPE"]
+    assert _lib.fa_fwd_tile(100, 96, 0, 0, 0, t) == codes["FA_ERR_HEADDIM"]
+    assert _lib.fa_fwd_tile(100, 64, 0, 5, 0, t) == codes["FA_ERR_DTYPE"]
+    assert _lib.fa_fwd_tile(100, 64, 0, _lib.FA_DTYPE_FP8_E4M3, _lib.FA_TILE_DROPOUT, t) == codes["FA_ERR_DTYPE"]
+
+
+def test_tile_query_honours_fa_tile(lib, monkeypatch):
+    """FA_TILE selects any shape compiled for the call's head dimension; one
+    compiled for the other head dimension, or an unknown string, falls back
+    to the default, and the query reports the fallback."""
+    for d in (64, 128):
+        monkeypatch.delenv("FA_TILE", raising=False)
+        default = _tile(300, d, False, _lib.FA_DTYPE_F16)
+        for tile, d64, d128 in _compiled_tiles():
+            monkeypatch.setenv("FA_TILE", tile)
+            ok = not (d64 and d != 64) and not (d128 and d != 128)
+            assert _tile(300, d, False, _lib.FA_DTYPE_F16) == (tile if ok else default), (tile, d)
+            # dropout kernels exist for the default shapes only: FA_TILE is ignored there
+            monkeypatch.delenv("FA_TILE")
+            want = _tile(300, d, False, _lib.FA_DTYPE_F16, _lib.FA_TILE_DROPOUT)
+            monkeypatch.setenv("FA_TILE", tile)
+            assert _tile(300, d, False, _lib.FA_DTYPE_F16, _lib.FA_TILE_DROPOUT) == want
+        monkeypatch.setenv("FA_TILE", "1x2x3x4x5")
+        assert _tile(300, d, False, _lib.FA_DTYPE_F16) == default
+
+
+def test_tile_query_defaults_are_compiled_shapes(lib, monkeypatch):
+    monkeypatch.delenv("FA_TILE", raising=False)
+    compiled = {t: (a, b) for t, a, b in _compiled_tiles()}
+    for d in (64, 128):
+        for dt in (_lib.FA_DTYPE_F16, _lib.FA_DTYPE_BF16, _lib.FA_DTYPE_FP8_E4M3):
+            for causal in (False, True):
+                for N in (1, 1000, 4096, 8192, 16384):
+                    modes = [_lib.FA_TILE_DENSE, _lib.FA_TILE_VARLEN]
+                    if dt != _lib.FA_DTYPE_FP8_E4M3:
+                        modes.append(_lib.FA_TILE_DROPOUT)
+                    for mode in modes:
+                        t = _tile(N, d, causal, dt, mode)
+                        d64, d128 = compiled[t]
+                        assert not (d64 and d != 64) and not (d128 and d != 128), (t, d)
+
+
+# ---- with the host stand-ins for the launchers (the sanitizer build of
+# tests/host_build), calls that pass validation are counted instead of
+# launched, so accepted edge cases can be driven without a GPU too.
+def _stub_counter(lib):
+    try:
+        return ctypes.c_int.in_dll(lib, "fa_stub_launches")
+    except ValueError:
+        return None
+
+
+@pytest.mark.parametrize("kw", [dict(), dict(N=1), dict(B=1, H=1, N=3), dict(scale=0.0), dict(scale=-2.5),
+                                dict(causal=1), dict(d=128, dtype=_lib.FA_DTYPE_BF16),
+                                dict(dtype=_lib.FA_DTYPE_FP8_E4M3), dict(stream=0x1234)])
+def test_accepted_calls_reach_the_launcher_once(lib, kw):
+    counter = _stub_counter(lib)
+    if counter is None:
+        pytest.skip("needs the host build whose launchers are stand-ins (FA_LIBRARY)")
+    before = counter.value
+    assert _call(**kw) == 0
+    assert counter.value == before + 1
+    assert _call8(**{k: v for k, v in kw.items() if k != "dtype"}) == 0
+    assert counter.value == before + 2
+

@@ -98,3 +98,23 @@ def test_bwd_larger_sampled(d, dtype, causal):
     x, g, dq, dk, dv = _grads(B, H, N, d, dtype, causal, scale, seed=9)
     worst = _check(x, g, dq, dk, dv, scale, causal, oracle.slice_sample(B, H, count=4))
     print(f"[bwd] worst normalised error {worst:.3g}")
+
+
+# (B, H, N, dtype, causal, slices checked).  At d = 128 the dK/dV kernel is
+# built for two waves per SIMD once the grid has at least 512 workgroups of
+# 128 rows (two per CU of the 256); every case here reaches that build, the
+# last at the shape its benchmark figures are quoted on.
+LARGE_D128 = [(2, 16, 2048, "bf16", False, 4), (2, 16, 2048, "bf16", True, 4), (2, 16, 2048, "f16", False, 4),
+              (2, 16, 2048, "f16", True, 4), (4, 32, 8192, "bf16", False, 2)]
+
+
+@pytest.mark.parametrize("B,H,N,dtype,causal,count", LARGE_D128,
+                         ids=[f"B{c[0]}H{c[1]}N{c[2]}-{c[3]}-{'causal' if c[4] else 'full'}" for c in LARGE_D128])
+def test_bwd_d128_large_grid(B, H, N, dtype, causal, count):
+    d = 128
+    assert -(-N // 128) * B * H >= 512  # the two-waves-per-SIMD dK/dV build runs
+    print(f"[bwd] d=128 large grid B={B} H={H} N={N} {dtype} causal={causal}", flush=True)
+    scale = 1 / math.sqrt(d)
+    x, g, dq, dk, dv = _grads(B, H, N, d, dtype, causal, scale, seed=21)
+    worst = _check(x, g, dq, dk, dv, scale, causal, oracle.slice_sample(B, H, count=count))
+    print(f"[bwd] worst normalised error {worst:.3g}")

@@ -214,3 +214,36 @@ def test_growing_scores_rescale(jumps, dtype, d, causal):
     x, scale = _growing_scores(B, H, N, d, dtype, jumps)
     o, lse = gu.run_gpu(x, scale, causal)
     gu.compare(x, gu.o_to_numpy(o), lse.cpu().numpy().astype(np.float64), scale, causal)
+
+
+@pytest.mark.parametrize("cfg", CONFIGS[1:], ids=[c[0] for c in CONFIGS[1:]])
+def test_full_size_exact_onehot(cfg):
+    """The configurations at full size, in the launch configuration the
+    benchmark times (default tile, whole grid), on inputs with an exact answer
+    for every row (``gen.onehot_blocks``: Q = 0, V one-hot by 8-key block,
+    shifted per slice).  lse must be ln(visible keys) on every row of every
+    slice: one key tile dropped or counted twice moves it by ln(N/(N-64)),
+    1/128 at N = 8192, which random inputs hide inside the 1e-3 bar.  O must be
+    the visible-key count of each column over the visible keys, to the output
+    rounding, on the 8 sampled slices: a lost or repeated 8-key block, or a
+    slice read in place of another, moves a column."""
+    name, B, H, N, d, dtype, causal, scale = cfg
+    tile = _lib.fwd_tile(N, d, causal, {"f16": 0, "bf16": 1, "fp8": 2}[dtype])
+    print(f"[onehot] {name} B={B} H={H} N={N} d={d} {dtype} causal={causal} tile={tile}", flush=True)
+    x = gen.onehot_blocks(B, H, N, d, dtype, block=8)
+    o, lse = gu.run_gpu(x, scale, causal)
+    n_vis = np.arange(1, N + 1, dtype=np.float64) if causal else np.full(N, float(N))
+    lse_np = lse.cpu().numpy().astype(np.float64)
+    err_l = np.abs(lse_np - np.log(n_vis)[None, None, :]).max()
+    assert err_l <= 1e-5 * math.log(N), f"max |lse - ln(visible keys)| = {err_l:.3g}"
+    worst = 0.0
+    for b, h in oracle.slice_sample(B, H):
+        v = oracle.dequantize(x.v[b, h], x.dtype, 1.0)
+        counts = np.cumsum(v, axis=0) if causal else np.broadcast_to(v.sum(axis=0), (N, d))
+        want = counts / n_vis[:, None]
+        got = o[b, h].float().cpu().numpy().astype(np.float64)
+        err = np.abs(got - want)
+        # one rounding to bfloat16 / binary16 (relative 2^-9 / 2^-12) of a value in [0, 1]
+        assert (err <= 2.0 ** -8 * want + 1e-6).all(), f"slice {(b, h)}: max|dO| = {err.max():.3g}"
+        worst = max(worst, float(err.max()))
+    print(f"[onehot] {name}: max|lse - ln n| = {err_l:.3g}, max|dO| on sampled slices = {worst:.3g}")

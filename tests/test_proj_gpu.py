@@ -123,12 +123,14 @@ def test_projection_then_attention(dtype, causal):
     assert do <= gu.O_TOL[dtype] and dl <= gu.LSE_TOL
 
 
-def test_projection_large_tile_sampled():
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_projection_large_tile_sampled(dtype):
     """A product large enough for the 256 x 256 tile (at least four
     workgroups per CU), with a partial token tile (M = 16000) and a partial
     feature tile (3 H d = 5760); every feature of 320 sampled tokens,
-    including the first and last ones, against the oracle."""
-    B, N, D, H, d, dtype = 4, 4000, 1024, 30, 64, "bf16"
+    including the first and last ones, against the oracle, for both 16-bit
+    types (each has its own instance of the tile)."""
+    B, N, D, H, d = 4, 4000, 1024, 30, 64
     print(f"[proj] large tile B={B} N={N} D={D} H={H} d={d} {dtype}", flush=True)
     pi = gen.make_projection(B, N, D, H, d, dtype, seed=5)
     outs = _run(pi)

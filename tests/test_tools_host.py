@@ -2,7 +2,6 @@
 every compiled tile shape from the kernel source, the GPU tile test covers
 each of them, and the profile recorder names its files and commands as
 documented."""
-import ast
 import os
 import sys
 
@@ -23,10 +22,50 @@ def test_sweep_reads_every_compiled_shape():
 
 
 def test_gpu_tile_test_covers_every_compiled_shape():
-    src = open(os.path.join(ROOT, "tests", "test_tiles_gpu.py")).read()
-    line = next(l for l in src.splitlines() if l.startswith("TILES = "))
-    listed = ast.literal_eval(line.split("=", 1)[1].strip())
-    assert sorted(listed) == sorted(sweep.variants())
+    from tests import test_tiles_gpu
+
+    listed = test_tiles_gpu.TILES
+    assert sorted(listed) == sorted(sweep.variants_per_d())
+    assert {t for _, t in listed} == set(sweep.variants())
+    for d, t in listed:  # a shape compiled for one head dimension only is tested there only
+        assert (d, t) in sweep.variants_per_d()
+
+
+def test_sweep_reads_the_instance_that_ran():
+    name = ("void fa::fa_fwd_kernel<fa::(anonymous namespace)::TrBF16, 128, true, 64, 8, 32, 1, 2, false>"
+            "(fa::FwdParams) [clone .kd]")
+    assert sweep.tile_of_kernel(name) == "64x8x32x1x2"
+    assert sweep.tile_of_kernel("void fa::fa_bwd_dq_kernel<...>") is None
+
+
+def test_profiler_crash_is_recorded_not_hidden(monkeypatch):
+    """A profiler run that ends with SIGSEGV is kept (its CSVs are complete)
+    but its exit status lands in the sweep row and the recorded summary;
+    any other failure raises."""
+    import subprocess
+
+    class P:
+        def __init__(self, rc):
+            self.returncode, self.stdout = rc, "{}"
+
+    for rc in (-11, 139):
+        monkeypatch.setattr(subprocess, "run", lambda *a, rc=rc, **k: P(rc))
+        crashes = []
+        sweep._run(["rocprofv3"], {}, 1, crashes)
+        assert crashes == [rc]
+        record.PROFILER_CRASHES.clear()
+        record._profile(["--kernel-trace"], [], "/tmp/x", "t")
+        assert record.PROFILER_CRASHES == [("--kernel-trace", rc)]
+        assert str(rc) in record._crash_note()
+    record.PROFILER_CRASHES.clear()
+    assert "0 for every run" in record._crash_note()
+    monkeypatch.setattr(subprocess, "run", lambda *a, **k: P(1))
+    import pytest
+
+    with pytest.raises(RuntimeError):
+        sweep._run(["rocprofv3"], {}, 1, [])
+    with pytest.raises(RuntimeError):
+        record._profile(["--kernel-trace"], [], "/tmp/x", "t")
 
 
 def test_record_tags_and_commands():

@@ -16,7 +16,7 @@ import torch
 import oracle
 from io_aware_attention_fwd_amd import _lib, gen
 from tests import gpu_util as gu
-from tests.test_tiles_gpu import TILES  # every compiled tile shape
+from tests.test_tiles_gpu import TILES  # (d, tile) of every shape compiled for d
 
 pytestmark = pytest.mark.gpu
 
@@ -161,15 +161,17 @@ def test_varlen_long_sequences_sampled(d, dtype, causal):
 # Every compiled tile shape (FA_TILE) on the mixed-length batch: the packed
 # addressing (sequence bounds, empty query tiles, rows past a sequence's end)
 # is shared by all of them.
-@pytest.mark.parametrize("tile", TILES)
-@pytest.mark.parametrize("d,dtype", [(64, "f16"), (128, "bf16")])
-def test_varlen_every_tile(tile, d, dtype):
+@pytest.mark.parametrize("d,tile", TILES, ids=[f"d{d}-{t}" for d, t in TILES])
+def test_varlen_every_tile(d, tile):
+    dtype = "f16" if d == 64 else "bf16"
     print(f"[varlen] tile {tile} d={d} {dtype}", flush=True)
     x, cu = gen.make_packed(LENGTHS, 2, d, dtype, seed=13)
     scale = 1 / math.sqrt(d)
     os.environ["FA_TILE"] = tile
     try:
         for causal in (False, True):
+            ran = _lib.fwd_tile(max(LENGTHS), d, causal, {"f16": 0, "bf16": 1}[dtype], _lib.FA_TILE_VARLEN)
+            assert ran == tile, f"FA_TILE={tile} requested, the library runs {ran}"
             o, lse = _run(x, cu, max(LENGTHS), scale, causal)
             _compare(x, cu, o, lse, scale, causal)
     finally:
