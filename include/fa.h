@@ -67,7 +67,8 @@ enum {
   FA_ERR_ALIGN = -6,    /* a tensor not 16-byte aligned, lse / cu_seqlens / delta not 4-byte, bias not 8-byte */
   FA_ERR_ALIAS = -7,    /* an output (o, lse; dq, dk, dv, delta; q, k, v of fa_qkv_proj) overlaps an input or another output */
   FA_ERR_HIP = -8,      /* the kernel launch reported a HIP error */
-  FA_ERR_DROPOUT = -9   /* fa_fwd_dropout: p_drop NaN, outside [0, 1), or keeping no score (t = 0) */
+  FA_ERR_DROPOUT = -9,  /* fa_fwd_dropout: p_drop NaN, outside [0, 1), or keeping no score (t = 0) */
+  FA_ERR_SCRATCH = -10  /* fa_bwd_noalloc: B * H * N above its static workspace (2^22 rows) */
 };
 
 /*
@@ -183,6 +184,29 @@ int fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
            const void* dout, void* dq, void* dk, void* dv, float* delta,
            int B, int H, int N, int d, float scale, int causal, int dtype, void* stream);
+
+/*
+ * fa_bwd_noalloc -- fa_bwd without the workspace argument, for callers that
+ * cannot allocate device memory or hand the library a workspace: code being
+ * captured into a HIP graph, tight serving loops, harnesses that forbid
+ * allocation.  The same kernels run; D = rowsum(dO * O) goes to a static
+ * device array of the library instead of `delta`.
+ *
+ *   Arguments as for fa_bwd, without delta.
+ *   Limit: B * H * N <= 2^22 (4 Mi rows, a 16 MiB array per GPU, reserved
+ *          from the library's load until the process ends); larger problems
+ *          return FA_ERR_SCRATCH before any HIP call.
+ * The array's device address on the GPU that `stream` belongs to (the
+ * current device for the null stream) is looked up on the first call for
+ * that GPU; the call allocates nothing, then or later.  Every row of D a
+ * call reads was written earlier in the same call, so nothing carries over
+ * from the previous call.  All calls on one GPU share that GPU's array:
+ * calls that may run at the same time on one GPU (different streams, or
+ * several host threads) race on it and must be serialised by the caller.
+ */
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                   const void* dout, void* dq, void* dk, void* dv,
+                   int B, int H, int N, int d, float scale, int causal, int dtype, void* stream);
 
 /*
  * fa_qkv_proj -- the fused input projection ahead of attention: page

@@ -1,7 +1,7 @@
 """ctypes binding of libfa.so: argument marshalling only.
 
 ``fa_fwd``, ``fa_fwd_fp8``, ``fa_fwd_varlen``, ``fa_fwd_dropout``, ``fa_bwd``,
-``fa_qkv_proj``, ``fa_fwd_tile``, ``fa_strerror`` and ``fa_version`` take the same arguments as
+``fa_bwd_noalloc``, ``fa_qkv_proj``, ``fa_fwd_tile``, ``fa_strerror`` and ``fa_version`` take the same arguments as
 the C functions declared in ``include/fa.h`` (device pointers as Python ints,
 the stream as a ``hipStream_t`` int or None).  ``fwd``, ``fwd_varlen``,
 ``fwd_dropout``, ``bwd`` and ``qkv_proj`` allocate
@@ -60,6 +60,8 @@ def load() -> ctypes.CDLL:
     lib.fa_fwd_dropout.restype = ci
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, cf, ci, ci, vp]
     lib.fa_bwd.restype = ci
+    lib.fa_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, cf, ci, ci, vp]
+    lib.fa_bwd_noalloc.restype = ci
     lib.fa_qkv_proj.argtypes = [vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, vp]
     lib.fa_qkv_proj.restype = ci
     lib.fa_fwd_tile.argtypes = [ci, ci, ci, ci, ci, ctypes.POINTER(ctypes.c_int)]
@@ -91,6 +93,10 @@ def fa_fwd_dropout(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, p_drop, se
 
 def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, scale, causal, dtype, stream) -> int:
     return load().fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, scale, int(causal), dtype, stream)
+
+
+def fa_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, scale, causal, dtype, stream) -> int:
+    return load().fa_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, scale, int(causal), dtype, stream)
 
 
 def fa_qkv_proj(x, w, bias, q, k, v, B, N, D, H, d, dtype, stream) -> int:

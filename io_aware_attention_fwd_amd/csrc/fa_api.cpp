@@ -125,10 +125,12 @@ int forward(const void* q, const void* k, const void* v, void* o, float* lse, co
   return FA_OK;
 }
 
+// delta == nullptr with `static_delta`: D goes to the library's static device
+// workspace (fa_bwd_noalloc), looked up after every argument check.
 int backward(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout, void* dq,
-             void* dk, void* dv, float* delta, int B, int H, int N, int d, float scale, int causal, int dtype,
-             void* stream) {
-  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !delta) return FA_ERR_NULL_PTR;
+             void* dk, void* dv, float* delta, bool static_delta, int B, int H, int N, int d, float scale, int causal,
+             int dtype, void* stream) {
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || (!delta && !static_delta)) return FA_ERR_NULL_PTR;
   if (dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
   if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
   if (d != 64 && d != 128) return FA_ERR_HEADDIM;
@@ -138,23 +140,26 @@ int backward(const void* q, const void* k, const void* v, const void* o, const f
   const int64_t n_blocks = ((int64_t)N + fa::kBwdRows - 1) / fa::kBwdRows;
   const int64_t total_wg = n_blocks * B * H;
   if (total_wg >= ((int64_t)1 << 31)) return FA_ERR_SHAPE;
+  if (static_delta && (int64_t)B * H * N > fa::kBwdScratchRows) return FA_ERR_SCRATCH;
   for (const void* ptr : {q, k, v, o, dout, (const void*)dq, (const void*)dk, (const void*)dv})
     if (!aligned(ptr, 16)) return FA_ERR_ALIGN;
-  if (!aligned(lse, 4) || !aligned(delta, 4)) return FA_ERR_ALIGN;
+  if (!aligned(lse, 4) || (!static_delta && !aligned(delta, 4))) return FA_ERR_ALIGN;
   const size_t t_bytes = (size_t)B * H * N * d * 2;
   const size_t r_bytes = (size_t)B * H * N * sizeof(float);
   const void* ins[] = {q, k, v, o, lse, dout};
   const size_t in_sz[] = {t_bytes, t_bytes, t_bytes, t_bytes, r_bytes, t_bytes};
   void* outs[] = {dq, dk, dv, delta};
   const size_t out_sz[] = {t_bytes, t_bytes, t_bytes, r_bytes};
-  for (int i = 0; i < 4; ++i) {
+  const int n_outs = static_delta ? 3 : 4;  // the static workspace overlaps nothing the caller owns
+  for (int i = 0; i < n_outs; ++i) {
     for (int j = 0; j < 6; ++j)
       if (overlap(outs[i], out_sz[i], ins[j], in_sz[j])) return FA_ERR_ALIAS;
-    for (int j = i + 1; j < 4; ++j)
+    for (int j = i + 1; j < n_outs; ++j)
       if (overlap(outs[i], out_sz[i], outs[j], out_sz[j])) return FA_ERR_ALIAS;
   }
   const double c = (double)scale * (double)kLog2e;
   if (!(fabs(c) <= (double)FLT_MAX)) return FA_ERR_SCALE;  // checked in double, before the float conversion
+  if (static_delta && fa::bwd_scratch(static_cast<hipStream_t>(stream), &delta) != hipSuccess) return FA_ERR_HIP;
   fa::BwdParams p;
   p.q = q;
   p.k = k;
@@ -278,7 +283,13 @@ int fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout, void* dq,
            void* dk, void* dv, float* delta, int B, int H, int N, int d, float scale, int causal, int dtype,
            void* stream) {
-  return backward(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, scale, causal, dtype, stream);
+  return backward(q, k, v, o, lse, dout, dq, dk, dv, delta, false, B, H, N, d, scale, causal, dtype, stream);
+}
+
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                   void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal, int dtype,
+                   void* stream) {
+  return backward(q, k, v, o, lse, dout, dq, dk, dv, nullptr, true, B, H, N, d, scale, causal, dtype, stream);
 }
 
 int fa_qkv_proj(const void* x, const void* w, const void* bias, void* q, void* k, void* v, int B, int N, int D, int H,
@@ -316,6 +327,7 @@ const char* fa_strerror(int code) {
     case FA_ERR_ALIAS: return "an output overlaps an input or the other output";
     case FA_ERR_HIP: return "the kernel launch reported a HIP error";
     case FA_ERR_DROPOUT: return "dropout rate outside [0, 1), NaN, or so close to 1 that no score is kept";
+    case FA_ERR_SCRATCH: return "B * H * N exceeds the static workspace of fa_bwd_noalloc (2^22 rows)";
     default: return "unknown error code";
   }
 }

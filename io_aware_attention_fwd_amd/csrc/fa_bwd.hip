@@ -26,6 +26,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "fa_device.h"
 #include "fa_launch.h"
 
@@ -438,6 +440,44 @@ hipError_t launch_bwd_dtype(int d, bool causal, const BwdParams& p, hipStream_t 
 }
 
 }  // namespace
+
+// D = rowsum(dO * O) of the allocation-free entry point (fa_bwd_noalloc):
+// kBwdScratchRows float32 rows (16 MiB), one copy per GPU, held until the
+// process ends.  Host code never passes this name to a kernel (on the host it
+// is only a stand-in for the symbol): the device address of each GPU's copy
+// comes from hipGetSymbolAddress, once per device, below.
+static __device__ __align__(256) float scratch[kBwdScratchRows];
+
+hipError_t bwd_scratch(hipStream_t stream, float** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static float* addr[kMaxDevices] = {};
+  int cur = 0, dev = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return e;
+  dev = cur;
+  if (stream != nullptr) {
+    e = hipStreamGetDevice(stream, &dev);  // the copy on the GPU the work is enqueued on
+    if (e != hipSuccess) return e;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    // the symbol's address is per device: look it up with that device current
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (dev != cur) {
+      const hipError_t r = hipSetDevice(cur);
+      if (e == hipSuccess) e = r;
+    }
+    if (e != hipSuccess) return e;
+    if (ptr == nullptr) return hipErrorInvalidSymbol;
+    addr[dev] = static_cast<float*>(ptr);
+  }
+  *out = addr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_bwd(Dtype dt, int d, bool causal, const BwdParams& p, hipStream_t stream) {
   if (d != 64 && d != 128) return hipErrorInvalidValue;

@@ -94,4 +94,12 @@ constexpr int kBwdRows = 128;
 // Enqueue the backward pass (dQ kernel, then dK/dV kernel, on one stream).
 hipError_t launch_bwd(Dtype dt, int d, bool causal, const BwdParams& p, hipStream_t stream);
 
+// Rows of D the allocation-free backward entry point holds in its static
+// device workspace (B * H * N at most): 2^22 float32 rows, 16 MiB per GPU.
+constexpr int64_t kBwdScratchRows = int64_t(1) << 22;
+
+// Device address of that workspace on the GPU `stream` belongs to (the
+// current device for the null stream), looked up once per device.
+hipError_t bwd_scratch(hipStream_t stream, float** out);
+
 }  // namespace fa

@@ -34,4 +34,11 @@ hipError_t launch_bwd(Dtype, int, bool, const BwdParams& p, hipStream_t) {
   return p.delta != nullptr ? hipSuccess : hipErrorInvalidValue;
 }
 
+// A stand-in address for the static workspace (never dereferenced here).
+hipError_t bwd_scratch(hipStream_t, float** out) {
+  static float stand_in[4];
+  *out = stand_in;
+  return hipSuccess;
+}
+
 }  // namespace fa

@@ -40,7 +40,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     declared = _declared_functions()
-    assert declared == ["fa_bwd", "fa_fwd", "fa_fwd_dropout", "fa_fwd_fp8", "fa_fwd_tile",
+    assert declared == ["fa_bwd", "fa_bwd_noalloc", "fa_fwd", "fa_fwd_dropout", "fa_fwd_fp8", "fa_fwd_tile",
                         "fa_fwd_varlen", "fa_qkv_proj", "fa_strerror", "fa_version"]
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.library_path()], capture_output=True, text=True, check=True).stdout
     exported = set(re.findall(r"\bT (fa_\w+)$", out, flags=re.M))
@@ -56,7 +56,7 @@ def test_version_matches_header(lib):
 
 def test_strerror_covers_every_code(lib):
     codes = _codes()
-    assert codes["FA_OK"] == 0 and len(codes) == 10
+    assert codes["FA_OK"] == 0 and len(codes) == 11
     texts = {_lib.fa_strerror(c) for c in codes.values()}
     assert len(texts) == len(codes) and "unknown error code" not in texts
     assert _lib.fa_strerror(12345) == "unknown error code"
@@ -344,3 +344,41 @@ def test_accepted_calls_reach_the_launcher_once(lib, kw):
     assert _call8(**{k: v for k, v in kw.items() if k != "dtype"}) == 0
     assert counter.value == before + 2
 
+
+# ---- fa_bwd_noalloc: fa_bwd without the workspace argument
+def _calln(**kw):
+    a = dict(q=BASE, k=BASE + SPAN, v=BASE + 2 * SPAN, o=BASE + 3 * SPAN, lse=BASE + 4 * SPAN, do=BASE + 5 * SPAN,
+             dq=BASE + 6 * SPAN, dk=BASE + 7 * SPAN, dv=BASE + 8 * SPAN,
+             B=2, H=4, N=1000, d=64, scale=0.125, causal=1, dtype=_lib.FA_DTYPE_F16, stream=None)
+    a.update(kw)
+    return _lib.fa_bwd_noalloc(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"], a["dv"],
+                               a["B"], a["H"], a["N"], a["d"], a["scale"], a["causal"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("case,kw,code", [
+    ("null dq", dict(dq=None), "FA_ERR_NULL_PTR"),
+    ("fp8", dict(dtype=_lib.FA_DTYPE_FP8_E4M3), "FA_ERR_DTYPE"),
+    ("N=0", dict(N=0), "FA_ERR_SHAPE"),
+    ("d=80", dict(d=80), "FA_ERR_HEADDIM"),
+    ("scale nan", dict(scale=math.nan), "FA_ERR_SCALE"),
+    ("scale huge", dict(scale=3e38), "FA_ERR_SCALE"),
+    ("one row past the workspace", dict(B=1, H=1, N=(1 << 22) + 1), "FA_ERR_SCRATCH"),
+    ("B*H*N past the workspace", dict(B=8, H=64, N=8193), "FA_ERR_SCRATCH"),
+    ("dk misaligned", dict(dk=BASE + 7 * SPAN + 8), "FA_ERR_ALIGN"),
+    ("dv inside v", dict(dv=BASE + 2 * SPAN + 1024), "FA_ERR_ALIAS"),
+    ("dq overlaps dk", dict(dq=BASE + 7 * SPAN - 64), "FA_ERR_ALIAS"),
+])
+@no_gpu
+def test_fa_bwd_noalloc_rejects(lib, case, kw, code):
+    assert _calln(**kw) == _codes()[code], case
+
+
+@pytest.mark.parametrize("kw", [dict(), dict(B=1, H=1, N=1 << 22), dict(B=4, H=32, N=8192, d=128),
+                                dict(dtype=_lib.FA_DTYPE_BF16, causal=0)])
+def test_noalloc_accepted_up_to_the_workspace(lib, kw):
+    counter = _stub_counter(lib)
+    if counter is None:
+        pytest.skip("needs the host build whose launchers are stand-ins (FA_LIBRARY)")
+    before = counter.value
+    assert _calln(**kw) == 0
+    assert counter.value == before + 1
