@@ -14,6 +14,7 @@ import shutil
 import subprocess
 import sys
 import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
@@ -24,7 +25,9 @@ ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}"]
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
-SOURCES = ["fa_fwd.hip", "fa_bwd.hip", "fa_proj.hip", "fa_api.cpp"]
+# (source, extra flags): the forward kernels are compiled once per dtype (FA_FWD_PART), side by side
+SOURCES = [("fa_fwd.hip", ["-DFA_FWD_PART=0"]), ("fa_fwd.hip", ["-DFA_FWD_PART=1"]),
+           ("fa_fwd.hip", ["-DFA_FWD_PART=2"]), ("fa_bwd.hip", []), ("fa_proj.hip", []), ("fa_api.cpp", [])]
 
 
 def _run(cmd):
@@ -40,14 +43,20 @@ def build(verbose: bool = False) -> str:
     """Compile and link libfa.so; return its path."""
     out_path = os.path.join(HERE, "libfa.so")
     with tempfile.TemporaryDirectory(prefix="fa_build_") as tmp:
-        objs = []
-        for src in SOURCES:
-            obj = os.path.join(tmp, src + ".o")
-            flags = COMMON + (DEVICE if src.endswith(".hip") else [f"--offload-arch={ARCH}"])
-            log = _run([HIPCC] + flags + ["-c", os.path.join(CSRC, src), "-o", obj])
-            if verbose and log:
-                print(log)
-            objs.append(obj)
+        objs = [os.path.join(tmp, f"{i}_{src}.o") for i, (src, _) in enumerate(SOURCES)]
+
+        def compile_one(entry, obj):
+            src, extra = entry
+            flags = COMMON + extra + (DEVICE if src.endswith(".hip") else [f"--offload-arch={ARCH}"])
+            return _run([HIPCC] + flags + ["-c", os.path.join(CSRC, src), "-o", obj])
+
+        # one compiler process per object, side by side
+        with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as pool:
+            logs = list(pool.map(compile_one, SOURCES, objs))
+        if verbose:
+            for log in logs:
+                if log:
+                    print(log)
         tmp_so = os.path.join(tmp, "libfa.so")
         _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp_so] + objs)
         staged = out_path + ".tmp"

@@ -106,6 +106,13 @@ __device__ __forceinline__ u32x4 philox4x32_10(u32 c0, u32 c1, u32 c2, u32 c3, u
   return u32x4{c0, c1, c2, c3};
 }
 
+// This lane's index in the wave, recomputed from the exec-independent lane
+// counter rather than kept in a register (used after long loops, where a
+// register holding it would be live all the way through).
+__device__ __forceinline__ int lane_id() {
+  return (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+}
+
 __device__ __forceinline__ float halves_max(float x) {
   u32 a = __builtin_bit_cast(u32, x), b = a;
   swap_halves(a, b);

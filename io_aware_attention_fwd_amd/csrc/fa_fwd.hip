@@ -318,6 +318,8 @@ __global__ __launch_bounds__(NW * 64, WPE) void fa_fwd_kernel(FwdParams p) {
       for (int qb = 0; qb < S::kQB; ++qb) {
         const int qi = qw0 + 32 * qb + l32;
         const int lim = CAUSAL ? min(qi, N - 1) : N - 1;  // last visible key
+        // element r of block kb holds key k0 + 32*kb + 8*(r/4) + 4*half + r%4; comparing the
+        // compile-time part of that offset with one per-lane bound needs no per-element address
 #pragma unroll
         for (int kb = 0; kb < S::kKB; ++kb)
 #pragma unroll
@@ -673,14 +675,17 @@ __global__ __launch_bounds__(NW * 64, WPE) void fa_fwd_kernel(FwdParams p) {
     }
   }
 
-  // ---- epilogue: combine the half-wave sums, normalise, store
+  // ---- epilogue: combine the half-wave sums, normalise, store.  The lane's
+  // position is recomputed here: registers holding it through the loop made
+  // the four-wave causal kernels spill.
+  const int e_lane = lane_id(), e_half = e_lane >> 5, e_l32 = e_lane & 31;
 #pragma unroll
   for (int qb = 0; qb < S::kQB; ++qb) {
-    const int qi = qw0 + 32 * qb + l32;
+    const int qi = qw0 + 32 * qb + e_l32;
     const float l_tot = halves_sum(lsum[qb]);
     const float inv = l_tot > 0.f ? p.o_mul / l_tot : 0.f;
     if (qi < N) {
-      if (half == 0)
+      if (e_half == 0)
         p.lse[(size_t)b * p.lse_batch + (size_t)h * p.lse_head + row0 + qi] =
             l_tot > 0.f ? (mref[qb] + __log2f(l_tot)) * kLn2 : -INFINITY;
       char* orow = (char*)p.o + (size_t)b * p.out_batch + (size_t)h * p.out_head + (size_t)(row0 + qi) * p.out_row;
@@ -688,7 +693,7 @@ __global__ __launch_bounds__(NW * 64, WPE) void fa_fwd_kernel(FwdParams p) {
       for (int db = 0; db < S::kDB; ++db)
 #pragma unroll
         for (int a4 = 0; a4 < 4; ++a4) {
-          const int col = 32 * db + 8 * a4 + 4 * half;
+          const int col = 32 * db + 8 * a4 + 4 * e_half;
           u32x2 w;
           w[0] = pack_p<kBf>(oacc[db][qb][4 * a4 + 0] * inv, oacc[db][qb][4 * a4 + 1] * inv);
           w[1] = pack_p<kBf>(oacc[db][qb][4 * a4 + 2] * inv, oacc[db][qb][4 * a4 + 3] * inv);
@@ -767,14 +772,36 @@ hipError_t dispatch_dtype(Dtype dt, int d, bool causal, const FwdParams& p, hipS
 
 }  // namespace
 
+// The instances of one dtype per object when FA_FWD_PART is 0, 1 or 2 (the
+// build compiles this file once per dtype, side by side); all of them when it
+// is undefined.
+#ifndef FA_FWD_PART
+#define FA_FWD_PART -1
+#endif
+#if FA_FWD_PART < 0 || FA_FWD_PART == 0
+hipError_t launch_fwd_f16(int d, bool causal, const FwdParams& p, hipStream_t stream) {
+  return dispatch_dtype<TrF16>(Dtype::F16, d, causal, p, stream);
+}
+
 hipError_t launch_fwd(Dtype dt, int d, bool causal, const FwdParams& p, hipStream_t stream) {
   if (d != 64 && d != 128) return hipErrorInvalidValue;
   switch (dt) {
-    case Dtype::F16: return dispatch_dtype<TrF16>(dt, d, causal, p, stream);
-    case Dtype::BF16: return dispatch_dtype<TrBF16>(dt, d, causal, p, stream);
-    case Dtype::FP8: return dispatch_dtype<TrFP8>(dt, d, causal, p, stream);
+    case Dtype::F16: return launch_fwd_f16(d, causal, p, stream);
+    case Dtype::BF16: return launch_fwd_bf16(d, causal, p, stream);
+    case Dtype::FP8: return launch_fwd_fp8(d, causal, p, stream);
   }
   return hipErrorInvalidValue;
 }
+#endif
+#if FA_FWD_PART < 0 || FA_FWD_PART == 1
+hipError_t launch_fwd_bf16(int d, bool causal, const FwdParams& p, hipStream_t stream) {
+  return dispatch_dtype<TrBF16>(Dtype::BF16, d, causal, p, stream);
+}
+#endif
+#if FA_FWD_PART < 0 || FA_FWD_PART == 2
+hipError_t launch_fwd_fp8(int d, bool causal, const FwdParams& p, hipStream_t stream) {
+  return dispatch_dtype<TrFP8>(Dtype::FP8, d, causal, p, stream);
+}
+#endif
 
 }  // namespace fa

@@ -84,6 +84,10 @@ enum class Dtype { F16 = 0, BF16 = 1, FP8 = 2 };
 
 // Enqueue one forward pass; returns hipSuccess or the launch error.
 hipError_t launch_fwd(Dtype dt, int d, bool causal, const FwdParams& p, hipStream_t stream);
+// The same for one dtype (the instances of each live in their own object).
+hipError_t launch_fwd_f16(int d, bool causal, const FwdParams& p, hipStream_t stream);
+hipError_t launch_fwd_bf16(int d, bool causal, const FwdParams& p, hipStream_t stream);
+hipError_t launch_fwd_fp8(int d, bool causal, const FwdParams& p, hipStream_t stream);
 
 // Enqueue the fused QKV projection (16-bit types; D a multiple of 64).
 hipError_t launch_qkv_proj(Dtype dt, const ProjParams& p, hipStream_t stream);
