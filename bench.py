@@ -8,7 +8,7 @@ B=8, H=32, N=1024, d=64 binary16 inputs, non-causal, scale 1/8, drawn i.i.d.
 N(0,1) from seed 0.  Inputs are resident in device memory before the timed
 region.  The shader clock needs tens of milliseconds of load to leave its
 idle level, so the GPU is first kept busy with plain device matmuls
-(``--clock-ms``, 100 by default; not the benchmarked call); then come W
+(``--clock-ms``, 150 by default; not the benchmarked call); then come W
 untimed warm-up steps (500 by default) and K timed steps (200 by default),
 timed with HIP events on the stream the kernel runs on, between two device
 synchronisations.
@@ -184,6 +184,8 @@ def condition_clock(ms):
         return
     a = torch.randn(2048, 2048, device="cuda", dtype=torch.float16)
     b = torch.empty_like(a)
+    torch.mm(a, a, out=b)  # the matmul library's first call sets itself up: kept out of the window
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
     while (time.perf_counter() - t0) * 1e3 < ms:
         for _ in range(8):
@@ -432,7 +434,7 @@ def main(argv=None):
     # headline reads ~20 % low; 500 and 2000 warm-up calls agree within 1 %.
     ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--no-sweep", action="store_true", help="skip the configurations and the N=512..8192 sweep")
-    ap.add_argument("--clock-ms", type=float, default=100.0,
+    ap.add_argument("--clock-ms", type=float, default=150.0,
                     help="milliseconds of device matmuls before the warm-up calls, to bring the shader clock "
                          "up from idle (0: none)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")

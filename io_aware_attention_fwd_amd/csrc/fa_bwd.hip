@@ -353,6 +353,12 @@ __global__ __launch_bounds__(256, WPE) void fa_bwd_dkdv_kernel(BwdParams p) {
     // casts: a bit cast of a vector element subscript reads element 0
     // whatever the index.)
     const bool need_mask = (qb0 + BQ > N) || (CAUSAL && qb0 < kw0 + 31);
+    // Element r holds query qb0 + 4*half + o(r), o(r) = 8*(r/4) + r%4: it is
+    // masked when o(r) >= q_end (past N) or, causal, when o(r) < k_rel (the
+    // query precedes this lane's key).  Two per-lane bounds against
+    // compile-time offsets, instead of each element's query index.
+    const int q_end = N - qb0 - 4 * half;
+    const int k_rel = key - qb0 - 4 * half;
     u32x4 pp[2], pds[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
@@ -370,8 +376,8 @@ __global__ __launch_bounds__(256, WPE) void fa_bwd_dkdv_kernel(BwdParams p) {
             const int r = 8 * t + 2 * e + j;  // = 4 * g + 2 * el + j
             float x = __builtin_fmaf(s[r], c, -l4[2 * el + j] * kLog2e);
             if (need_mask) {
-              const int query = qb0 + 8 * (r >> 2) + 4 * half + (r & 3);
-              if (query >= N || (CAUSAL && key > query)) x = -INFINITY;
+              const int o = 8 * (r >> 2) + (r & 3);
+              if (o >= q_end || (CAUSAL && o < k_rel)) x = -INFINITY;
             }
             pr[j] = __builtin_amdgcn_exp2f(x);
             ds[j] = pr[j] * (dp[r] - d4[2 * el + j]);
@@ -403,9 +409,12 @@ __global__ __launch_bounds__(256, WPE) void fa_bwd_dkdv_kernel(BwdParams p) {
     }
   }
 
-  if (key < N) {
-    store_rowT<kBf, D>((char*)p.dk + base + (size_t)key * B::kRow, dkacc, half, p.scale);
-    store_rowT<kBf, D>((char*)p.dv + base + (size_t)key * B::kRow, dvacc, half, 1.f);
+  // the lane's key and half-wave are recomputed here rather than kept in
+  // registers through the loop (which made the causal build spill)
+  const int e_lane = lane_id(), e_key = kw0 + (e_lane & 31), e_half = e_lane >> 5;
+  if (e_key < N) {
+    store_rowT<kBf, D>((char*)p.dk + base + (size_t)e_key * B::kRow, dkacc, e_half, p.scale);
+    store_rowT<kBf, D>((char*)p.dv + base + (size_t)e_key * B::kRow, dvacc, e_half, 1.f);
   }
 }
 

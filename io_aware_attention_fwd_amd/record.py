@@ -49,9 +49,10 @@ HEADLINE = (8, 32, 1024, 64, "f16", False)
 SQ_COUNTERS = ["SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CU_CYCLES",
                "SQ_ACTIVE_INST_VALU", "SQ_WAVE_CYCLES", "SQ_WAIT_INST_LDS", "GRBM_GUI_ACTIVE"]
 # instruction counts (per wave, summed over the dispatch) behind the vector-ALU ceiling bench.py reports:
-# all vector ALU instructions (matrix ones included), the transcendental ones, the matrix ones, LDS ones
+# vector ALU instructions, the transcendental ones among them, matrix instructions, LDS instructions, and
+# the bytes LDS loads returned (in 64-byte units)
 INSTR_COUNTERS = {"valu": "SQ_INSTS_VALU", "valu_trans": "SQ_INSTS_VALU_TRANS_F32", "mfma": "SQ_INSTS_MFMA",
-                  "lds": "SQ_INSTS_LDS"}
+                  "lds": "SQ_INSTS_LDS", "lds_load_64b": "SQ_INSTS_LDS_LOAD_BANDWIDTH"}
 MODE_FAMILY = {"varlen": "fwd", "dropout": "fwd", "bwd": "bwd", "proj": "proj"}
 
 

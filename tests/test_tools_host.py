@@ -17,7 +17,7 @@ def test_sweep_reads_every_compiled_shape():
     assert len(v) == len(set(v)) >= 5
     for t in v:
         qw, nw, bc, sched, wpe = (int(x) for x in t.split("x"))
-        assert qw in (32, 64) and bc in (32, 64) and sched in (0, 1) and 1 <= wpe <= 4
+        assert qw in (32, 64) and bc in (32, 64) and sched in (0, 1, 2) and 1 <= wpe <= 4
         assert sched == 0 or nw in (8, 16)  # the ping-pong groups hold NW/8 waves of every SIMD
 
 
