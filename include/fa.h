@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define FA_VERSION 300 /* major * 10000 + minor * 100 + patch: 0.3.0 */
+#define FA_VERSION 400 /* major * 10000 + minor * 100 + patch: 0.4.0 */
 
 /* Storage format of q, k, v. */
 typedef enum {
