@@ -42,9 +42,14 @@ def library_path() -> str:
 def load() -> ctypes.CDLL:
     """Load libfa.so once; raise if it has not been built."""
     global _LIB
-    if _LIB is not None:
-        return _LIB
-    path = library_path()
+    if _LIB is None:
+        _LIB = open_library(library_path())
+    return _LIB
+
+
+def open_library(path: str) -> ctypes.CDLL:
+    """A handle on one build of the library (libfa.so, or libfa_sync.so with its
+    extra barriers) with every entry point's argument types set."""
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'`")
     lib = ctypes.CDLL(path)
@@ -70,7 +75,6 @@ def load() -> ctypes.CDLL:
     lib.fa_strerror.restype = ctypes.c_char_p
     lib.fa_version.argtypes = []
     lib.fa_version.restype = ci
-    _LIB = lib
     return lib
 
 

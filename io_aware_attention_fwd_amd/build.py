@@ -3,7 +3,10 @@
     python -m io_aware_attention_fwd_amd.build
 
 Compiles every source under ``csrc/`` on each call (no staleness check) and
-atomically replaces ``libfa.so`` next to this file.  hipcc cross-compiles, so
+atomically replaces ``libfa.so`` next to this file, and ``libfa_sync.so``:
+the same sources with ``FA_SYNC_CHECK`` (extra waits and workgroup barriers
+at points every wave reaches), whose results the GPU tests require to equal
+``libfa.so``'s bit for bit.  hipcc cross-compiles, so
 no GPU is needed.  All device code is built with packed-fp32 instructions
 disabled.
 """
@@ -39,30 +42,37 @@ def _run(cmd):
     return out
 
 
-def build(verbose: bool = False) -> str:
-    """Compile and link libfa.so; return its path."""
-    out_path = os.path.join(HERE, "libfa.so")
-    with tempfile.TemporaryDirectory(prefix="fa_build_") as tmp:
-        objs = [os.path.join(tmp, f"{i}_{src}.o") for i, (src, _) in enumerate(SOURCES)]
+# (library name, extra flags for every object)
+LIBRARIES = [("libfa.so", []), ("libfa_sync.so", ["-DFA_SYNC_CHECK"])]
 
-        def compile_one(entry, obj):
-            src, extra = entry
+
+def build(verbose: bool = False) -> str:
+    """Compile and link libfa.so and its barrier-checking twin; return libfa.so's path."""
+    with tempfile.TemporaryDirectory(prefix="fa_build_") as tmp:
+        jobs = [(lib, src, extra + lib_extra, os.path.join(tmp, f"{lib}_{i}_{src}.o"))
+                for lib, lib_extra in LIBRARIES for i, (src, extra) in enumerate(SOURCES)]
+
+        def compile_one(job):
+            _, src, extra, obj = job
             flags = COMMON + extra + (DEVICE if src.endswith(".hip") else [f"--offload-arch={ARCH}"])
             return _run([HIPCC] + flags + ["-c", os.path.join(CSRC, src), "-o", obj])
 
         # one compiler process per object, side by side
-        with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as pool:
-            logs = list(pool.map(compile_one, SOURCES, objs))
+        with ThreadPoolExecutor(max_workers=min(len(jobs), os.cpu_count() or 1)) as pool:
+            logs = list(pool.map(compile_one, jobs))
         if verbose:
             for log in logs:
                 if log:
                     print(log)
-        tmp_so = os.path.join(tmp, "libfa.so")
-        _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp_so] + objs)
-        staged = out_path + ".tmp"
-        shutil.copyfile(tmp_so, staged)
-        os.replace(staged, out_path)
-    return out_path
+        for lib, _ in LIBRARIES:
+            tmp_so = os.path.join(tmp, lib)
+            _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp_so] +
+                 [obj for l, _, _, obj in jobs if l == lib])
+            out_path = os.path.join(HERE, lib)
+            staged = out_path + ".tmp"
+            shutil.copyfile(tmp_so, staged)
+            os.replace(staged, out_path)
+    return os.path.join(HERE, "libfa.so")
 
 
 if __name__ == "__main__":

@@ -255,7 +255,9 @@ __global__ __launch_bounds__(256, WPE) void fa_bwd_dq_kernel(BwdParams p) {
       issue_rows_vl<D, NW, BC>(rk, lds_k1, (kt + 1) * BC, wave, lane);
       issue_rows_k<D, NW, BC>(rv, lds_v1, (kt + 1) * BC, wave, lane);
     }
+    FA_SYNC_POINT();
     step(kt, lds_k0, lds_v0);
+    FA_SYNC_POINT();
     if (kt + 1 < n_kv) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
@@ -263,7 +265,9 @@ __global__ __launch_bounds__(256, WPE) void fa_bwd_dq_kernel(BwdParams p) {
         issue_rows_vl<D, NW, BC>(rk, lds_k0, (kt + 2) * BC, wave, lane);
         issue_rows_k<D, NW, BC>(rv, lds_v0, (kt + 2) * BC, wave, lane);
       }
+      FA_SYNC_POINT();
       step(kt + 1, lds_k1, lds_v1);
+      FA_SYNC_POINT();
     }
   }
 
@@ -400,12 +404,16 @@ __global__ __launch_bounds__(256, WPE) void fa_bwd_dkdv_kernel(BwdParams p) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (qt + 1 < n_qt) issue(qt + 1, lds_q1, lds_d1, lds_ld1);
+    FA_SYNC_POINT();
     step(qt, lds_q0, lds_d0, lds_ld0);
+    FA_SYNC_POINT();
     if (qt + 1 < n_qt) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
       if (qt + 2 < n_qt) issue(qt + 2, lds_q0, lds_d0, lds_ld0);
+      FA_SYNC_POINT();
       step(qt + 1, lds_q1, lds_d1, lds_ld1);
+      FA_SYNC_POINT();
     }
   }
 

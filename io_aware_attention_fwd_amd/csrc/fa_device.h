@@ -7,6 +7,23 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+// Debug build (compiled with FA_SYNC_CHECK): full memory waits and a
+// workgroup barrier at extra points that every wave of a workgroup reaches.
+// The kernels' results must not change, bit for bit; a difference against
+// the normal build exposes a missing wait or barrier (there is no LDS race
+// checker on this platform).
+#ifdef FA_SYNC_CHECK
+#define FA_SYNC_POINT()                                            \
+  do {                                                             \
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");    \
+    __syncthreads();                                               \
+  } while (0)
+#else
+#define FA_SYNC_POINT() \
+  do {                  \
+  } while (0)
+#endif
+
 namespace fa {
 namespace {
 

@@ -184,6 +184,8 @@ __global__ __launch_bounds__(NW * 64, WPE) void fa_fwd_kernel(FwdParams p) {
     }
   }
 
+  FA_SYNC_POINT();  // (debug build) Q in registers and LDS before anything else
+
   // B operand of query block qb, instruction step s (16-bit values)
   auto qop = [&](int qb, int s) __attribute__((always_inline)) {
     return kQ1Lds && qb == 1 ? lds_read_b128(lds_q1, q1base + 32 * s) : q16[qb][s];
@@ -613,6 +615,7 @@ __global__ __launch_bounds__(NW * 64, WPE) void fa_fwd_kernel(FwdParams p) {
   auto tile_step = [&](int kt, const char* lk, const char* lv_prev, char* k_next, char* v_cur) __attribute__((always_inline)) {
     if (kt + 1 < n_kv) issue_k(kt + 1, k_next);
     if (kt < n_kv) issue_v(kt, v_cur);
+    FA_SYNC_POINT();
     if (group == 0) {
       mfma_phase(kt, lk, lv_prev);
     } else if (active(kt - 1)) {
@@ -647,6 +650,7 @@ __global__ __launch_bounds__(NW * 64, WPE) void fa_fwd_kernel(FwdParams p) {
         issue_k(kt + 1, kn);
         issue_v(kt + 1, vn);
       }
+      FA_SYNC_POINT();
       if (active(kt)) {
         if constexpr (WPE >= 4) {
           // Four waves per SIMD leave 128 registers: each operand is read
@@ -666,6 +670,7 @@ __global__ __launch_bounds__(NW * 64, WPE) void fa_fwd_kernel(FwdParams p) {
           mma_pv();
         }
       }
+      FA_SYNC_POINT();
     };
     issue_k(0, lds_k0);
     issue_v(0, lds_v0);
@@ -675,6 +680,7 @@ __global__ __launch_bounds__(NW * 64, WPE) void fa_fwd_kernel(FwdParams p) {
     }
   }
 
+  FA_SYNC_POINT();
   // ---- epilogue: combine the half-wave sums, normalise, store.  The lane's
   // position is recomputed here: registers holding it through the loop made
   // the four-wave causal kernels spill.
