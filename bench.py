@@ -503,7 +503,9 @@ def main(argv=None):
     from io_aware_attention_fwd_amd import _lib
 
     def point(pb, ph, n, dd, dt, cz, x=None):
-        """Time one workload (after a 50 ms warm-up of its own); returns (entry, inputs)."""
+        """Time one workload (after a 50 ms warm-up of its own); returns (entry, call, kept), where
+        kept holds the host inputs and the device tensors the call's raw pointers refer to: the
+        caller keeps it alive for as long as it may launch the call again."""
         c2, st2, keep2 = make_call(pb, ph, n, dd, dt, cz, 1.0 / math.sqrt(dd), x=x)
         warm(c2)
         fl2 = flops(pb, ph, n, dd, cz)
@@ -513,7 +515,7 @@ def main(argv=None):
         e = {"B": pb, "H": ph, "N": n, "d": dd, "dtype": dt, "causal": cz, "tile": tile, **r,
              "peak_tflops": PEAK_TFLOPS[dt], "algorithmic_bytes": ab,
              "algorithmic_hbm_gbs": round(ab / (r["ms_median"] * 1e-3) / 1e9, 1)}
-        return e, keep2[0], c2
+        return e, c2, keep2
 
     configs, sweep = [], []
     clocks = None
@@ -521,7 +523,8 @@ def main(argv=None):
         # the five configurations, each a first-class entry with its own roofline figures and oracle baseline
         for tag, pb, ph, n, dd, dt, cz in CONFIGS:
             progress(f"config {tag} B={pb} H={ph} N={n} d={dd} {dt} causal={int(cz)}")
-            e, x2, c2 = point(pb, ph, n, dd, dt, cz)
+            e, c2, kept = point(pb, ph, n, dd, dt, cz)
+            x2 = kept[0]
             fl2 = flops(pb, ph, n, dd, cz)
             rec = load_record(record_tag(pb, ph, n, dd, dt, cz))
             e = {"config": tag, **e,
@@ -549,7 +552,7 @@ def main(argv=None):
                     e["cpu_baseline"] = cpu_baseline_sampled(x2, cz, 1.0 / math.sqrt(dd), args.cpu_budget / 3,
                                                              oracle.slice_sample(pb, ph))
             configs.append(e)
-            del x2, c2
+            del x2, c2, kept  # the call is not launched again: its tensors may go
             torch.cuda.empty_cache()
         # the benchmark page's forward-time table shape (B=8, H=32, d=64, N=512..8192, no mask) and the
         # N >= 4096 head-dimension 64/128 points, causal and bfloat16 too (c2 and c4 are entries above)
@@ -558,8 +561,9 @@ def main(argv=None):
                    (B, H, 8192, 128, "bf16", False), (B, H, 8192, 128, "bf16", True)]
         for pb, ph, n, dd, dt, cz in points:
             progress(f"sweep point B={pb} H={ph} N={n} d={dd} {dt} causal={int(cz)}")
-            e, _, _ = point(pb, ph, n, dd, dt, cz)
+            e, _, kept = point(pb, ph, n, dd, dt, cz)
             sweep.append(e)
+            del kept
             torch.cuda.empty_cache()
     if clocks is None:
         def busy():
