@@ -58,7 +58,8 @@ int forward(const void* q, const void* k, const void* v, void* o, float* lse, co
   const int64_t in_row = packed ? (int64_t)L.H * d * eb : (int64_t)d * eb;
   if ((int64_t)(L.N + br) * in_row >= ((int64_t)1 << 31)) return FA_ERR_SHAPE;
   const int64_t n_qtiles = ((int64_t)L.N + br - 1) / br;
-  const int64_t total_wg = n_qtiles * L.B * L.H;
+  // dense causal grids: one workgroup per pair of query tiles (the kernel's two jobs)
+  const int64_t total_wg = (causal && !packed ? (n_qtiles + 1) / 2 : n_qtiles) * L.B * L.H;
   if (total_wg >= ((int64_t)1 << 31)) return FA_ERR_SHAPE;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4) ||
       (packed && !aligned(L.cu, 4)))

@@ -23,7 +23,7 @@ struct FwdParams {
   int B, H, N;    // N: rows per sequence (dense) or the longest sequence (packed)
   int total;      // packed layout: rows of the packed tensors
   int n_qtiles;   // ceil(N / rows per workgroup)
-  int total_wg;   // n_qtiles * B * H
+  int total_wg;   // workgroups: n_qtiles * B * H, or ceil(n_qtiles / 2) * B * H for dense causal grids
   long long in_batch, in_head;    // byte strides of Q, K, V
   int in_row;
   long long out_batch, out_head;  // byte strides of O

@@ -33,36 +33,39 @@ inline constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 // matrix phase is bound by the LDS operand reads (1 KB per instruction of a
 // 32-row wave).  64-row waves with 32-key tiles cut them (to half for fp8,
 // whose Q operands fit in registers, and to three quarters at 16 bits, whose
-// second query block's Q operands are read from LDS): without the causal
-// mask +11 % for fp8 and +6 to +8 % for the 16-bit types (B8 H32 N4096 /
-// N8192, B4 H32 N8192).  With the causal mask the 512-row workgroups wait on
-// their longest waves: bfloat16 gains only at N = 16384 (+5 %, against a tie
-// at 8192 and -4 % at 4096), and fp8 keeps the plain schedule at two waves
-// per SIMD.  At d = 64 the softmax's vector work per tile is as long as the
+// second query block's Q operands are read from LDS): without the causal mask
+// +11 % for fp8 and +6 to +8 % for the 16-bit types (B8 H32 N4096 / N8192, B4
+// H32 N8192).  With the causal mask (each workgroup runs a long and a short
+// query tile) the same shape wins from 4096 rows on for the 16-bit types (+1 %
+// at 4096, +2 to +3 % at 8192 and 16384) and from 8192 for fp8 (+4 %); below
+// that 256-row ping-pong workgroups win at 2048 rows, and the 128-row plain
+// shape at two waves per SIMD at 1024 rows and fewer (+8 to +16 %) and for fp8
+// below 8192.  At d = 64 the softmax's vector work per tile is as long as the
 // tile's matrix work, and a single wave issues vector instructions at well
 // under the SIMD's rate, so the shapes that keep more waves in their softmax
 // at once win: 32 rows per wave at four waves per SIMD.  Without a causal
-// mask, 8 such waves per workgroup (each K/V tile in LDS then serves 256
-// query rows, half the tile loads per row of 4 waves) for binary16 and fp8
-// at every length and for bfloat16 below 4096 rows; from 4096 rows on,
-// bfloat16 (whose row sums take twice the vector work) prefers 64-row
-// ping-pong waves (twice the matrix work per LDS operand) and fp8 the plain
-// 64-row shape, both by a few percent.  With the causal mask the 4-wave
-// workgroups win: a workgroup waits for its longest wave, and the causal
-// row lengths differ more across 256 rows.  Packed batches of mixed lengths
-// (N = the longest) keep 128-row workgroups: larger ones
-// idle most of their waves on the short sequences (lengths 256..4096: 660
-// against 596 TFLOP/s at d = 64, 726 against 699 at d = 128).  Dropout
-// kernels exist for the shapes listed in dispatch_dropout.
+// mask, 8 such waves per workgroup (each K/V tile in LDS then serves 256 query
+// rows, half the tile loads per row of 4 waves) for binary16 and fp8 at every
+// length and for bfloat16 below 4096 rows; from 4096 rows on, bfloat16 (whose
+// row sums take twice the vector work) prefers 64-row ping-pong waves (twice
+// the matrix work per LDS operand) and fp8 the plain 64-row shape, both by a
+// few percent.  With the causal mask the 4-wave workgroups at four waves per
+// SIMD win for every type (for fp8 by 1 to 5 % over three waves per SIMD, 512
+// to 16384 rows).  Packed batches of mixed lengths (N = the longest) keep
+// 128-row workgroups: larger ones idle most of their waves on the short
+// sequences (lengths 256..4096: 660 against 596 TFLOP/s at d = 64, 726 against
+// 699 at d = 128).  Dropout kernels exist for the shapes listed in
+// dispatch_dropout.
 inline int default_variant(Dtype dt, int d, bool causal, int N, bool dropout, bool packed) {
   if (packed && !dropout) return d == 128 ? 3 : dt == Dtype::FP8 ? 2 : 1;
   if (d == 128) {
     if (dropout) return 0;  // the one d = 128 shape compiled with dropout
-    if (dt == Dtype::FP8) return causal ? 3 : 8;
-    return !causal || N >= 16384 ? 8 : 0;
+    if (!causal) return 8;
+    if (dt == Dtype::FP8) return N >= 8192 ? 8 : 3;
+    return N >= 4096 ? 8 : N >= 2048 ? 0 : 3;
   }
   if (dropout) return !causal && N >= 1024 ? 4 : 2;
-  if (causal) return dt == Dtype::FP8 ? 2 : 1;
+  if (causal) return 1;
   if (N >= 4096 && dt != Dtype::F16) return dt == Dtype::FP8 ? 4 : 5;
   return 7;
 }
