@@ -27,6 +27,7 @@
 #include <stdint.h>
 
 #include <mutex>
+#include <type_traits>
 
 #include "fa_device.h"
 #include "fa_launch.h"
@@ -37,13 +38,35 @@ namespace {
 constexpr float kLog2e = 1.44269504088896341f;
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// A 16-bit tile that is read both by rows (128-bit reads: 16 consecutive
+// rows x 16 bytes per cycle) and transposed: the V layout of fa_device.h plus
+// a 16-byte pad after every 4 rows.  Row r = 4a + b then starts at 64b + 16a
+// bytes modulo 256 at both row sizes, so the 16 rows of a row read land on
+// 16 different 4-bank groups, while each 4-row group of a transposing read
+// still fills the four 64-byte quarters.  In the V layout alone rows r, r+4,
+// r+8 and r+12 share their banks (a four-way conflict on every row read).
+template <int RB>
+struct RowsLayout {
+  using V = VLayout<RB, false>;
+  static_assert(4 % V::kGroupRows == 0, "the V layout's groups divide 4 rows");
+  static constexpr int kGroupRows = 4;
+  __host__ __device__ static constexpr int row(int r) { return V::row(r) + 16 * (r >> 2); }
+  static constexpr int kGroupBytes = row(kGroupRows);  // bytes from one group to the next
+};
+
 template <int D>
 struct BwdShape {
   static constexpr int kDB = D / 32;      // 32-wide blocks of the head dimension
   static constexpr int kSteps = D / 16;   // 16-wide k-steps of a product over d
   static constexpr int kRow = 2 * D;      // bytes per row (16-bit elements)
   static constexpr int kCR = kRow / 16;   // 16-byte chunks per row
-  using VL = VLayout<kRow, false>;
+  // Q, dO (dK/dV kernel) and K (dQ kernel) tiles are read by rows and
+  // transposed.  At d = 128 they take the conflict-free RowsLayout (+2 %
+  // without the causal mask, +6 % with it, B4 H32 N8192).  At d = 64 it
+  // measured +3 % without the mask but -2 to -3 % with it (the
+  // three-waves-per-SIMD causal dK/dV kernel then spills), so d = 64 keeps
+  // the V layout.
+  using VL = std::conditional_t<D == 128, RowsLayout<kRow>, VLayout<kRow, false>>;
   static constexpr int kGV = VL::kGroupBytes / 16;  // LDS granules per group of rows
   static constexpr int kRSK = kRow + 16;            // padded row of a tile read by rows only
 };
