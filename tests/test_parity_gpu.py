@@ -216,6 +216,26 @@ def test_growing_scores_rescale(jumps, dtype, d, causal):
     gu.compare(x, gu.o_to_numpy(o), lse.cpu().numpy().astype(np.float64), scale, causal)
 
 
+# The mirror image for the causal grid, whose workgroups walk their shorter
+# query tile's keys down from the diagonal: scores fall along the keys, so the
+# first tiles such a walk visits hold the smallest scores and every tile
+# further down raises the rows' maxima (by 7: accepted against the earlier
+# references; by 30: rescaled; the mix: both, and tiles that lower them).
+# N = 1189 gives an odd number of query tiles and a ragged last one for
+# 128-, 256- and 512-row workgroups alike (one workgroup runs a lone middle
+# tile).
+@pytest.mark.parametrize("jumps", [[-7.0] * 19, [-30.0], [-3.0, -7.0, -25.0, 0.0, -40.0, 9.0]],
+                         ids=["fall7", "fall30", "mixed"])
+@pytest.mark.parametrize("dtype,d", [("f16", 64), ("bf16", 64), ("fp8", 64), ("f16", 128), ("bf16", 128)])
+def test_falling_scores_downward_walk(jumps, dtype, d):
+    B, H, N = 1, 2, 1189
+    print(f"[falling] jumps={jumps} {dtype} d={d} tile={_lib.fwd_tile(N, d, True, {'f16': 0, 'bf16': 1, 'fp8': 2}[dtype])}",
+          flush=True)
+    x, scale = _growing_scores(B, H, N, d, dtype, jumps)
+    o, lse = gu.run_gpu(x, scale, True)
+    gu.compare(x, gu.o_to_numpy(o), lse.cpu().numpy().astype(np.float64), scale, True)
+
+
 @pytest.mark.parametrize("cfg", CONFIGS[1:], ids=[c[0] for c in CONFIGS[1:]])
 def test_full_size_exact_onehot(cfg):
     """The configurations at full size, in the launch configuration the
