@@ -102,10 +102,12 @@ def test_bwd_larger_sampled(d, dtype, causal):
 
 # (B, H, N, dtype, causal, slices checked).  At d = 128 the dK/dV kernel is
 # built for two waves per SIMD once the grid has at least 512 workgroups of
-# 128 rows (two per CU of the 256); every case here reaches that build, the
-# last at the shape its benchmark figures are quoted on.
+# 128 rows (two per CU of the 256); every case here reaches that build, N =
+# 1000 with a ragged last block, the last at the shape its benchmark figures
+# are quoted on.
 LARGE_D128 = [(2, 16, 2048, "bf16", False, 4), (2, 16, 2048, "bf16", True, 4), (2, 16, 2048, "f16", False, 4),
-              (2, 16, 2048, "f16", True, 4), (4, 32, 8192, "bf16", False, 2)]
+              (2, 16, 2048, "f16", True, 4), (4, 32, 1000, "bf16", True, 4), (4, 32, 1000, "f16", False, 4),
+              (4, 32, 8192, "bf16", False, 2)]
 
 
 @pytest.mark.parametrize("B,H,N,dtype,causal,count", LARGE_D128,

@@ -111,12 +111,15 @@ def test_varlen_and_dropout_identical(libs):
         _same(outs[0][0], outs[1][0], f"dropout O d={d}")
 
 
-@pytest.mark.parametrize("d,dtype", [(64, "f16"), (64, "bf16"), (128, "f16"), (128, "bf16")])
+# (B, H): small grids, and at d = 128 one of at least 512 workgroups of 128
+# rows, where the dK/dV kernel is built for two waves per SIMD
+@pytest.mark.parametrize("d,dtype,B,H", [(64, "f16", 2, 4), (64, "bf16", 2, 4), (128, "f16", 2, 4), (128, "bf16", 2, 4),
+                                         (128, "bf16", 4, 32)])
 @pytest.mark.parametrize("N", [300, 1000])
-def test_backward_identical(libs, d, dtype, N):
-    print(f"[sync] backward d={d} {dtype} N={N}", flush=True)
-    x = gen.make(2, 4, N, d, dtype, seed=25)
-    g = gen.make(2, 4, N, d, dtype, seed=26)
+def test_backward_identical(libs, d, dtype, B, H, N):
+    print(f"[sync] backward B={B} H={H} d={d} {dtype} N={N}", flush=True)
+    x = gen.make(B, H, N, d, dtype, seed=25)
+    g = gen.make(B, H, N, d, dtype, seed=26)
     q, k, v = gu.to_device(x)
     do = gu.to_device(g)[0]
     for causal in (False, True):
