@@ -182,12 +182,19 @@ __global__ __launch_bounds__(256, WPE) void fa_bwd_dq_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) char lds_v1[kSV];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, half = lane >> 5, l32 = lane & 31;
+  // Causal grids at d = 64 pair query blocks n-1-i and i of a slice in one
+  // workgroup, as the forward kernel does: the long block walks its keys up
+  // from key 0, the short one down from its diagonal, so the workgroups of a
+  // slice have equal work and read the same K/V tile at about the same time
+  // (+1 to +14 %, most at small N).  At d = 128 it measured -1 to +2 %, so
+  // query blocks run one per workgroup there, longest first.
+  constexpr bool kPair = CAUSAL && D == 64;
   const int tile = xcd_remap(blockIdx.x, p.total_wg);
-  const int bh = tile / p.n_blocks;
-  int qt = tile - bh * p.n_blocks;
-  if (CAUSAL) qt = p.n_blocks - 1 - qt;
+  const int per_slice = kPair ? (p.n_blocks + 1) / 2 : p.n_blocks;
+  const int bh = tile / per_slice;
+  const int pair = tile - bh * per_slice;
+  const int n_jobs = kPair && 2 * pair + 1 < p.n_blocks ? 2 : 1;
   const int N = p.N;
-  const int q0 = qt * kBwdRows, qw0 = q0 + wave * 32, qi = qw0 + l32;
   const u32 slice = (u32)N * B::kRow;
   const size_t base = (size_t)bh * N * B::kRow;
   const auto rq = make_rsrc((const char*)p.q + base, slice);
@@ -195,106 +202,115 @@ __global__ __launch_bounds__(256, WPE) void fa_bwd_dq_kernel(BwdParams p) {
   const auto rv = make_rsrc((const char*)p.v + base, slice);
   const auto ro = make_rsrc((const char*)p.o + base, slice);
   const auto rdo = make_rsrc((const char*)p.dout + base, slice);
-
-  // this lane's query row: Q and dO as matrix operands, D = dO . O, lse
-  u32x4 q16[B::kSteps], do16[B::kSteps], o16[B::kSteps];
-  load_row_operand<D>(rq, qi, half, q16);
-  load_row_operand<D>(rdo, qi, half, do16);
-  load_row_operand<D>(ro, qi, half, o16);
-  float dpart = 0.f;
-#pragma unroll
-  for (int s = 0; s < B::kSteps; ++s)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) dpart = dot_pair<kBf>(do16[s][e], o16[s][e], dpart);
-  const float Dq = halves_sum(dpart);
-  const float Lq = qi < N ? p.lse[(size_t)bh * N + qi] * kLog2e : 0.f;
-  if (half == 0 && qi < N) p.delta[(size_t)bh * N + qi] = Dq;
   const float c = p.c;
 
-  const int n_all = (N + BC - 1) / BC;
-  const int n_kv = CAUSAL ? min(n_all, (q0 + kBwdRows - 1) / BC + 1) : n_all;
-  const bool has_rows = qw0 < N;
+  for (int job = 0; job < n_jobs; ++job) {
+    const int qt = !CAUSAL ? pair : job == 0 ? p.n_blocks - 1 - pair : pair;  // longest first
+    const bool down = kPair && job == 1;  // keys from the diagonal down to key 0
+    if (job > 0) __syncthreads();          // the first block's LDS stages are free again
+    const int q0 = qt * kBwdRows, qw0 = q0 + wave * 32, qi = qw0 + l32;
 
-  f32x16 dqacc[B::kDB];
+    // this lane's query row: Q and dO as matrix operands, D = dO . O, lse
+    u32x4 q16[B::kSteps], do16[B::kSteps], o16[B::kSteps];
+    load_row_operand<D>(rq, qi, half, q16);
+    load_row_operand<D>(rdo, qi, half, do16);
+    load_row_operand<D>(ro, qi, half, o16);
+    float dpart = 0.f;
 #pragma unroll
-  for (int db = 0; db < B::kDB; ++db) dqacc[db] = f32x16{};
-  const int kbase = B::VL::row(l32) + 16 * half;  // row operand of the K tile (grouped layout)
-  const int vbase = l32 * B::kRSK + 16 * half;    // row operand of the V tile (padded rows)
-  const int tbase = tr_base<D>(lane);
+    for (int s = 0; s < B::kSteps; ++s)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dpart = dot_pair<kBf>(do16[s][e], o16[s][e], dpart);
+    const float Dq = halves_sum(dpart);
+    const float Lq = qi < N ? p.lse[(size_t)bh * N + qi] * kLog2e : 0.f;
+    if (half == 0 && qi < N) p.delta[(size_t)bh * N + qi] = Dq;
 
-  auto step = [&](int kt, const char* lk, const char* lv) __attribute__((always_inline)) {
-    if (!has_rows || (CAUSAL && kt * BC > qw0 + 31)) return;
-    f32x16 st[kKB], dpt[kKB];
+    const int n_all = (N + BC - 1) / BC;
+    const int n_kv = CAUSAL ? min(n_all, (q0 + kBwdRows - 1) / BC + 1) : n_all;
+    // key tile of step i (steps are counted in the order the tiles are visited)
+    auto ktile = [&](int i) __attribute__((always_inline)) { return down ? n_kv - 1 - i : i; };
+    const bool has_rows = qw0 < N;
+
+    f32x16 dqacc[B::kDB];
 #pragma unroll
-    for (int kb = 0; kb < kKB; ++kb) {
-      st[kb] = f32x16{};
-      dpt[kb] = f32x16{};
+    for (int db = 0; db < B::kDB; ++db) dqacc[db] = f32x16{};
+    const int kbase = B::VL::row(l32) + 16 * half;  // row operand of the K tile (grouped layout)
+    const int vbase = l32 * B::kRSK + 16 * half;    // row operand of the V tile (padded rows)
+    const int tbase = tr_base<D>(lane);
+
+    auto step = [&](int kt, const char* lk, const char* lv) __attribute__((always_inline)) {
+      if (!has_rows || (CAUSAL && ktile(kt) * BC > qw0 + 31)) return;
+      f32x16 st[kKB], dpt[kKB];
 #pragma unroll
-      for (int s = 0; s < B::kSteps; ++s) {
-        const u32x4 ka = lds_read_b128(lk, kbase + B::VL::row(32 * kb) + 32 * s);
-        st[kb] = mfma16(ka, q16[s], st[kb], kBf);
-        const u32x4 va = lds_read_b128(lv, vbase + 32 * kb * B::kRSK + 32 * s);
-        dpt[kb] = mfma16(va, do16[s], dpt[kb], kBf);
-      }
-    }
-    const int k0 = kt * BC;
-    const int lim = CAUSAL ? min(qi, N - 1) : N - 1;  // last key this query sees
-    const bool need_mask = (k0 + BC > N) || (CAUSAL && k0 + BC - 1 > qw0);
-    u32x4 pb[kKB][2];
+      for (int kb = 0; kb < kKB; ++kb) {
+        st[kb] = f32x16{};
+        dpt[kb] = f32x16{};
 #pragma unroll
-    for (int kb = 0; kb < kKB; ++kb)
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float ds[2];
-#pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const int r = 8 * t + 2 * e + j;
-            float x = __builtin_fmaf(st[kb][r], c, -Lq);
-            if (need_mask) {
-              const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-              if (key > lim) x = -INFINITY;
-            }
-            const float pr = __builtin_amdgcn_exp2f(x);
-            ds[j] = pr * (dpt[kb][r] - Dq);
-          }
-          pb[kb][t][e] = pack_p<kBf>(ds[0], ds[1]);
+        for (int s = 0; s < B::kSteps; ++s) {
+          const u32x4 ka = lds_read_b128(lk, kbase + B::VL::row(32 * kb) + 32 * s);
+          st[kb] = mfma16(ka, q16[s], st[kb], kBf);
+          const u32x4 va = lds_read_b128(lv, vbase + 32 * kb * B::kRSK + 32 * s);
+          dpt[kb] = mfma16(va, do16[s], dpt[kb], kBf);
         }
-#pragma unroll
-    for (int db = 0; db < B::kDB; ++db)
+      }
+      const int k0 = ktile(kt) * BC;
+      const int lim = CAUSAL ? min(qi, N - 1) : N - 1;  // last key this query sees
+      const bool need_mask = (k0 + BC > N) || (CAUSAL && k0 + BC - 1 > qw0);
+      u32x4 pb[kKB][2];
 #pragma unroll
       for (int kb = 0; kb < kKB; ++kb)
 #pragma unroll
-        for (int t = 0; t < 2; ++t) dqacc[db] = mfma16(tr_operand<D>(lk, tbase, db, kb, t), pb[kb][t], dqacc[db], kBf);
-  };
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float ds[2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+              const int r = 8 * t + 2 * e + j;
+              float x = __builtin_fmaf(st[kb][r], c, -Lq);
+              if (need_mask) {
+                const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+                if (key > lim) x = -INFINITY;
+              }
+              const float pr = __builtin_amdgcn_exp2f(x);
+              ds[j] = pr * (dpt[kb][r] - Dq);
+            }
+            pb[kb][t][e] = pack_p<kBf>(ds[0], ds[1]);
+          }
+#pragma unroll
+      for (int db = 0; db < B::kDB; ++db)
+#pragma unroll
+        for (int kb = 0; kb < kKB; ++kb)
+#pragma unroll
+          for (int t = 0; t < 2; ++t) dqacc[db] = mfma16(tr_operand<D>(lk, tbase, db, kb, t), pb[kb][t], dqacc[db], kBf);
+    };
 
-  issue_rows_vl<D, NW, BC>(rk, lds_k0, 0, wave, lane);
-  issue_rows_k<D, NW, BC>(rv, lds_v0, 0, wave, lane);
-  for (int kt = 0; kt < n_kv; kt += 2) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (kt + 1 < n_kv) {
-      issue_rows_vl<D, NW, BC>(rk, lds_k1, (kt + 1) * BC, wave, lane);
-      issue_rows_k<D, NW, BC>(rv, lds_v1, (kt + 1) * BC, wave, lane);
-    }
-    FA_SYNC_POINT();
-    step(kt, lds_k0, lds_v0);
-    FA_SYNC_POINT();
-    if (kt + 1 < n_kv) {
+    issue_rows_vl<D, NW, BC>(rk, lds_k0, ktile(0) * BC, wave, lane);
+    issue_rows_k<D, NW, BC>(rv, lds_v0, ktile(0) * BC, wave, lane);
+    for (int kt = 0; kt < n_kv; kt += 2) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
-      if (kt + 2 < n_kv) {
-        issue_rows_vl<D, NW, BC>(rk, lds_k0, (kt + 2) * BC, wave, lane);
-        issue_rows_k<D, NW, BC>(rv, lds_v0, (kt + 2) * BC, wave, lane);
+      if (kt + 1 < n_kv) {
+        issue_rows_vl<D, NW, BC>(rk, lds_k1, ktile(kt + 1) * BC, wave, lane);
+        issue_rows_k<D, NW, BC>(rv, lds_v1, ktile(kt + 1) * BC, wave, lane);
       }
       FA_SYNC_POINT();
-      step(kt + 1, lds_k1, lds_v1);
+      step(kt, lds_k0, lds_v0);
       FA_SYNC_POINT();
+      if (kt + 1 < n_kv) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (kt + 2 < n_kv) {
+          issue_rows_vl<D, NW, BC>(rk, lds_k0, ktile(kt + 2) * BC, wave, lane);
+          issue_rows_k<D, NW, BC>(rv, lds_v0, ktile(kt + 2) * BC, wave, lane);
+        }
+        FA_SYNC_POINT();
+        step(kt + 1, lds_k1, lds_v1);
+        FA_SYNC_POINT();
+      }
     }
-  }
 
-  if (qi < N) store_rowT<kBf, D>((char*)p.dq + base + (size_t)qi * B::kRow, dqacc, half, p.scale);
+    if (qi < N) store_rowT<kBf, D>((char*)p.dq + base + (size_t)qi * B::kRow, dqacc, half, p.scale);
+  }
 }
 
 // ------------------------------------------------------------ dK/dV kernel
@@ -315,11 +331,21 @@ __global__ __launch_bounds__(256, WPE) void fa_bwd_dkdv_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) float lds_ld1[2 * BQ];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, half = lane >> 5, l32 = lane & 31;
+  // Causal grids at d = 64 pair key blocks i (its queries run to the end:
+  // the longest) and n-1-i of a slice in one workgroup.  The long block
+  // walks its query tiles down from the last one and the short block up
+  // from its diagonal, so the workgroups of a slice have equal work and read
+  // the same query tile at about the same time.  At d = 128 the kernel has
+  // no register to spare for the second block's state (its query-tile loop
+  // reloads spilled offsets), so key blocks run one per workgroup, longest
+  // first, as the dQ kernel's query blocks do there.
+  constexpr bool kPair = CAUSAL && D == 64;
   const int tile = xcd_remap(blockIdx.x, p.total_wg);
-  const int bh = tile / p.n_blocks;
-  const int kblk = tile - bh * p.n_blocks;
+  const int per_slice = kPair ? (p.n_blocks + 1) / 2 : p.n_blocks;
+  const int bh = tile / per_slice;
+  const int pair = tile - bh * per_slice;
+  const int n_jobs = kPair && 2 * pair + 1 < p.n_blocks ? 2 : 1;
   const int N = p.N;
-  const int k0 = kblk * kBwdRows, kw0 = k0 + wave * 32, key = kw0 + l32;
   const u32 slice = (u32)N * B::kRow;
   const size_t base = (size_t)bh * N * B::kRow;
   const auto rq = make_rsrc((const char*)p.q + base, slice);
@@ -328,131 +354,144 @@ __global__ __launch_bounds__(256, WPE) void fa_bwd_dkdv_kernel(BwdParams p) {
   const auto rdo = make_rsrc((const char*)p.dout + base, slice);
   const auto rl = make_rsrc(p.lse + (size_t)bh * N, (u32)N * 4);
   const auto rd = make_rsrc(p.delta + (size_t)bh * N, (u32)N * 4);
-
-  // this lane's key row of K and V as matrix operands
-  u32x4 k16[B::kSteps], v16[B::kSteps];
-  load_row_operand<D>(rk, key, half, k16);
-  load_row_operand<D>(rv, key, half, v16);
   const float c = p.c;
-
-  f32x16 dkacc[B::kDB], dvacc[B::kDB];
-#pragma unroll
-  for (int db = 0; db < B::kDB; ++db) {
-    dkacc[db] = f32x16{};
-    dvacc[db] = f32x16{};
-  }
-  const int rbase = B::VL::row(l32) + 16 * half;  // row operand of a Q or dO tile
-  const int tbase = tr_base<D>(lane);
   const int n_qt = (N + BQ - 1) / BQ;
-  const int qt0 = CAUSAL ? k0 / BQ : 0;  // earlier queries see none of this block's keys
-  const bool has_keys = kw0 < N;
 
-  // wave 0 fetches the tile's 32 lse values (lanes 0..7, into dst[0..31]) and
-  // its 32 D values (lanes 8..15, into dst[32..63]): a direct load writes
-  // lane L's 16 bytes at dst + 16*L
-  auto issue_ld = [&](int qt, float* dst) __attribute__((always_inline)) {
-    if (wave == 0) {
-      const int r = qt * BQ + 4 * (lane & 7);
-      if (lane < 8) load_lds16(rl, (char*)dst, r * 4);
-      if (lane >= 8 && lane < 16) load_lds16(rd, (char*)dst, r * 4);
-    }
-  };
-  auto issue = [&](int qt, char* dq_tile, char* ddo_tile, float* dld) __attribute__((always_inline)) {
-    issue_rows_vl<D, NW, BQ>(rq, dq_tile, qt * BQ, wave, lane);
-    issue_rows_vl<D, NW, BQ>(rdo, ddo_tile, qt * BQ, wave, lane);
-    issue_ld(qt, dld);
-  };
+  for (int job = 0; job < n_jobs; ++job) {
+    const int kblk = job == 0 ? pair : p.n_blocks - 1 - pair;
+    const bool down = kPair && job == 0;  // query tiles from the last one down to the diagonal
+    if (job > 0) __syncthreads();          // the first block's LDS stages are free again
+    const int k0 = kblk * kBwdRows, kw0 = k0 + wave * 32, key = kw0 + l32;
 
-  auto step = [&](int qt, const char* tq, const char* tdo, const float* tld) __attribute__((always_inline)) {
-    const int qb0 = qt * BQ;
-    if (!has_keys || (CAUSAL && qb0 + BQ - 1 < kw0)) return;  // no query of the tile sees these keys
-    f32x16 s = f32x16{}, dp = f32x16{};
+    // this lane's key row of K and V as matrix operands
+    u32x4 k16[B::kSteps], v16[B::kSteps];
+    load_row_operand<D>(rk, key, half, k16);
+    load_row_operand<D>(rv, key, half, v16);
+
+    f32x16 dkacc[B::kDB], dvacc[B::kDB];
 #pragma unroll
-    for (int st = 0; st < B::kSteps; ++st) {
-      const u32x4 qa = lds_read_b128(tq, rbase + 32 * st);
-      s = mfma16(qa, k16[st], s, kBf);
-      const u32x4 da = lds_read_b128(tdo, rbase + 32 * st);
-      dp = mfma16(da, v16[st], dp, kBf);
+    for (int db = 0; db < B::kDB; ++db) {
+      dkacc[db] = f32x16{};
+      dvacc[db] = f32x16{};
     }
-    // Element r of the accumulators belongs to query row 8*(r/4) + 4*half +
-    // r%4 of the tile; the four rows of group r/4 take their lse and D from
-    // one 128-bit LDS read each, right where they are used.  (Whole-vector
-    // casts: a bit cast of a vector element subscript reads element 0
-    // whatever the index.)
-    const bool need_mask = (qb0 + BQ > N) || (CAUSAL && qb0 < kw0 + 31);
-    // Element r holds query qb0 + 4*half + o(r), o(r) = 8*(r/4) + r%4: it is
-    // masked when o(r) >= q_end (past N) or, causal, when o(r) < k_rel (the
-    // query precedes this lane's key).  Two per-lane bounds against
-    // compile-time offsets, instead of each element's query index.
-    const int q_end = N - qb0 - 4 * half;
-    const int k_rel = key - qb0 - 4 * half;
-    u32x4 pp[2], pds[2];
+    const int rbase = B::VL::row(l32) + 16 * half;  // row operand of a Q or dO tile
+    const int tbase = tr_base<D>(lane);
+    const int qt0 = CAUSAL ? k0 / BQ : 0;  // earlier queries see none of this block's keys
+    const int n_steps = max(n_qt - qt0, 0);
+    // query tile of step i (steps are counted in the order the tiles are visited)
+    auto qtile = [&](int i) __attribute__((always_inline)) { return down ? n_qt - 1 - i : qt0 + i; };
+    const bool has_keys = kw0 < N;
+
+    // wave 0 fetches the tile's 32 lse values (lanes 0..7, into dst[0..31]) and
+    // its 32 D values (lanes 8..15, into dst[32..63]): a direct load writes
+    // lane L's 16 bytes at dst + 16*L
+    auto issue_ld = [&](int qt, float* dst) __attribute__((always_inline)) {
+      if (wave == 0) {
+        const int r = qt * BQ + 4 * (lane & 7);
+        if (lane < 8) load_lds16(rl, (char*)dst, r * 4);
+        if (lane >= 8 && lane < 16) load_lds16(rd, (char*)dst, r * 4);
+      }
+    };
+    auto issue = [&](int qt, char* dq_tile, char* ddo_tile, float* dld) __attribute__((always_inline)) {
+      issue_rows_vl<D, NW, BQ>(rq, dq_tile, qt * BQ, wave, lane);
+      issue_rows_vl<D, NW, BQ>(rdo, ddo_tile, qt * BQ, wave, lane);
+      issue_ld(qt, dld);
+    };
+
+    auto step = [&](int i, const char* tq, const char* tdo, const float* tld) __attribute__((always_inline)) {
+      const int qb0 = qtile(i) * BQ;
+      if (!has_keys || (CAUSAL && qb0 + BQ - 1 < kw0)) return;  // no query of the tile sees these keys
+      f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+      for (int st = 0; st < B::kSteps; ++st) {
+        const u32x4 qa = lds_read_b128(tq, rbase + 32 * st);
+        s = mfma16(qa, k16[st], s, kBf);
+        const u32x4 da = lds_read_b128(tdo, rbase + 32 * st);
+        dp = mfma16(da, v16[st], dp, kBf);
+      }
+      // Element r of the accumulators belongs to query row 8*(r/4) + 4*half +
+      // r%4 of the tile; the four rows of group r/4 take their lse and D from
+      // one 128-bit LDS read each, right where they are used.  (Whole-vector
+      // casts: a bit cast of a vector element subscript reads element 0
+      // whatever the index.)
+      const bool need_mask = (qb0 + BQ > N) || (CAUSAL && qb0 < kw0 + 31);
+      // Element r holds query qb0 + 4*half + o(r), o(r) = 8*(r/4) + r%4: it is
+      // masked when o(r) >= q_end (past N) or, causal, when o(r) < k_rel (the
+      // query precedes this lane's key).  Two per-lane bounds against
+      // compile-time offsets, instead of each element's query index.
+      const int q_end = N - qb0 - 4 * half;
+      const int k_rel = key - qb0 - 4 * half;
+      u32x4 pp[2], pds[2];
 #pragma unroll
-      for (int eh = 0; eh < 2; ++eh) {
-        const int g = 2 * t + eh;
-        const f32x4 l4 = __builtin_bit_cast(f32x4, lds_read_b128((const char*)tld, (8 * g + 4 * half) * 4));
-        const f32x4 d4 = __builtin_bit_cast(f32x4, lds_read_b128((const char*)tld, (BQ + 8 * g + 4 * half) * 4));
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int el = 0; el < 2; ++el) {
-          const int e = 2 * eh + el;
-          float pr[2], ds[2];
+        for (int eh = 0; eh < 2; ++eh) {
+          const int g = 2 * t + eh;
+          const f32x4 l4 = __builtin_bit_cast(f32x4, lds_read_b128((const char*)tld, (8 * g + 4 * half) * 4));
+          const f32x4 d4 = __builtin_bit_cast(f32x4, lds_read_b128((const char*)tld, (BQ + 8 * g + 4 * half) * 4));
 #pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const int r = 8 * t + 2 * e + j;  // = 4 * g + 2 * el + j
-            float x = __builtin_fmaf(s[r], c, -l4[2 * el + j] * kLog2e);
-            if (need_mask) {
-              const int o = 8 * (r >> 2) + (r & 3);
-              if (o >= q_end || (CAUSAL && o < k_rel)) x = -INFINITY;
+          for (int el = 0; el < 2; ++el) {
+            const int e = 2 * eh + el;
+            float pr[2], ds[2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+              const int r = 8 * t + 2 * e + j;  // = 4 * g + 2 * el + j
+              float x = __builtin_fmaf(s[r], c, -l4[2 * el + j] * kLog2e);
+              if (need_mask) {
+                const int o = 8 * (r >> 2) + (r & 3);
+                if (o >= q_end || (CAUSAL && o < k_rel)) x = -INFINITY;
+              }
+              pr[j] = __builtin_amdgcn_exp2f(x);
+              ds[j] = pr[j] * (dp[r] - d4[2 * el + j]);
             }
-            pr[j] = __builtin_amdgcn_exp2f(x);
-            ds[j] = pr[j] * (dp[r] - d4[2 * el + j]);
+            pp[t][e] = pack_p<kBf>(pr[0], pr[1]);
+            pds[t][e] = pack_p<kBf>(ds[0], ds[1]);
           }
-          pp[t][e] = pack_p<kBf>(pr[0], pr[1]);
-          pds[t][e] = pack_p<kBf>(ds[0], ds[1]);
         }
-      }
 #pragma unroll
-    for (int db = 0; db < B::kDB; ++db)
+      for (int db = 0; db < B::kDB; ++db)
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        dvacc[db] = mfma16(tr_operand<D>(tdo, tbase, db, 0, t), pp[t], dvacc[db], kBf);
-        dkacc[db] = mfma16(tr_operand<D>(tq, tbase, db, 0, t), pds[t], dkacc[db], kBf);
-      }
-  };
+        for (int t = 0; t < 2; ++t) {
+          dvacc[db] = mfma16(tr_operand<D>(tdo, tbase, db, 0, t), pp[t], dvacc[db], kBf);
+          dkacc[db] = mfma16(tr_operand<D>(tq, tbase, db, 0, t), pds[t], dkacc[db], kBf);
+        }
+    };
 
-  if (qt0 < n_qt) issue(qt0, lds_q0, lds_d0, lds_ld0);
-  for (int qt = qt0; qt < n_qt; qt += 2) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (qt + 1 < n_qt) issue(qt + 1, lds_q1, lds_d1, lds_ld1);
-    FA_SYNC_POINT();
-    step(qt, lds_q0, lds_d0, lds_ld0);
-    FA_SYNC_POINT();
-    if (qt + 1 < n_qt) {
+    if (n_steps > 0) issue(qtile(0), lds_q0, lds_d0, lds_ld0);
+    for (int i = 0; i < n_steps; i += 2) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
-      if (qt + 2 < n_qt) issue(qt + 2, lds_q0, lds_d0, lds_ld0);
+      if (i + 1 < n_steps) issue(qtile(i + 1), lds_q1, lds_d1, lds_ld1);
       FA_SYNC_POINT();
-      step(qt + 1, lds_q1, lds_d1, lds_ld1);
+      step(i, lds_q0, lds_d0, lds_ld0);
       FA_SYNC_POINT();
+      if (i + 1 < n_steps) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (i + 2 < n_steps) issue(qtile(i + 2), lds_q0, lds_d0, lds_ld0);
+        FA_SYNC_POINT();
+        step(i + 1, lds_q1, lds_d1, lds_ld1);
+        FA_SYNC_POINT();
+      }
     }
-  }
 
-  // the lane's key and half-wave are recomputed here rather than kept in
-  // registers through the loop (which made the causal build spill)
-  const int e_lane = lane_id(), e_key = kw0 + (e_lane & 31), e_half = e_lane >> 5;
-  if (e_key < N) {
-    store_rowT<kBf, D>((char*)p.dk + base + (size_t)e_key * B::kRow, dkacc, e_half, p.scale);
-    store_rowT<kBf, D>((char*)p.dv + base + (size_t)e_key * B::kRow, dvacc, e_half, 1.f);
+    // the lane's key and half-wave are recomputed here rather than kept in
+    // registers through the loop (which made the causal build spill)
+    const int e_lane = lane_id(), e_key = kw0 + (e_lane & 31), e_half = e_lane >> 5;
+    if (e_key < N) {
+      store_rowT<kBf, D>((char*)p.dk + base + (size_t)e_key * B::kRow, dkacc, e_half, p.scale);
+      store_rowT<kBf, D>((char*)p.dv + base + (size_t)e_key * B::kRow, dvacc, e_half, 1.f);
+    }
   }
 }
 
 namespace {
 
 template <class Tr, int D, bool CAUSAL>
-hipError_t launch_bwd_typed(const BwdParams& p, hipStream_t stream) {
+hipError_t launch_bwd_typed(const BwdParams& bp, hipStream_t stream) {
+  // causal grids at d = 64: one workgroup per pair of 128-row blocks
+  BwdParams p = bp;
+  if (CAUSAL && D == 64) p.total_wg = (bp.n_blocks + 1) / 2 * bp.B * bp.H;
   hipLaunchKernelGGL((fa_bwd_dq_kernel<Tr, D, CAUSAL, D == 64 ? 4 : 2, D == 64 ? 32 : 64>), dim3(p.total_wg), dim3(256), 0,
                      stream, p);
   hipError_t e = hipGetLastError();
@@ -465,10 +504,10 @@ hipError_t launch_bwd_typed(const BwdParams& p, hipStream_t stream) {
   if constexpr (D == 64) {
     hipLaunchKernelGGL((fa_bwd_dkdv_kernel<Tr, D, CAUSAL, 3>), dim3(p.total_wg), dim3(256), 0, stream, p);
   } else {
-    if (p.total_wg >= 512)
-      hipLaunchKernelGGL((fa_bwd_dkdv_kernel<Tr, D, CAUSAL, 2>), dim3(p.total_wg), dim3(256), 0, stream, p);
+    if (bp.total_wg >= 512)
+      hipLaunchKernelGGL((fa_bwd_dkdv_kernel<Tr, D, CAUSAL, 2>), dim3(bp.total_wg), dim3(256), 0, stream, bp);
     else
-      hipLaunchKernelGGL((fa_bwd_dkdv_kernel<Tr, D, CAUSAL, 1>), dim3(p.total_wg), dim3(256), 0, stream, p);
+      hipLaunchKernelGGL((fa_bwd_dkdv_kernel<Tr, D, CAUSAL, 1>), dim3(bp.total_wg), dim3(256), 0, stream, bp);
   }
   return hipGetLastError();
 }
