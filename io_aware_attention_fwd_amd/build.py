@@ -28,9 +28,11 @@ ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}"]
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
-# (source, extra flags): the forward kernels are compiled once per dtype (FA_FWD_PART), side by side
+# (source, extra flags): the forward kernels are compiled in four parts (FA_FWD_PART: one per dtype
+# and the pre-scaled binary16 instances), side by side
 SOURCES = [("fa_fwd.hip", ["-DFA_FWD_PART=0"]), ("fa_fwd.hip", ["-DFA_FWD_PART=1"]),
-           ("fa_fwd.hip", ["-DFA_FWD_PART=2"]), ("fa_bwd.hip", []), ("fa_proj.hip", []), ("fa_api.cpp", [])]
+           ("fa_fwd.hip", ["-DFA_FWD_PART=2"]), ("fa_fwd.hip", ["-DFA_FWD_PART=3"]), ("fa_bwd.hip", []),
+           ("fa_proj.hip", []), ("fa_api.cpp", [])]
 
 
 def _run(cmd):

@@ -38,12 +38,18 @@
 //     one softmax step whose vector work this removes from most tiles.
 //   * Causal: tiles right of a wave's last row are skipped; tiles that cross
 //     the diagonal (and the ragged last tile) are masked element-wise.
-//   * exp is v_exp_f32 (exp2) with scale * log2(e) folded into one fma.
+//   * exp is v_exp_f32 (exp2) with scale * log2(e) folded into one fma; for
+//     binary16 at d = 64, where the vector work bounds the kernel, Q is
+//     multiplied by scale * log2(e) as it is loaded and each score
+//     accumulator starts at minus its row's reference, so the matrix
+//     instructions deliver the exponent directly.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
+
+#include <type_traits>
 
 #include "fa_device.h"
 #include "fa_launch.h"
@@ -84,7 +90,19 @@ struct Shape {
   static_assert(BC % 32 == 0, "whole 32-key blocks");
 };
 
+// Binary16 inputs whose Q the kernel multiplies by c = scale * log2(e) and
+// rounds to binary16 as it loads it (relative error 2^-11 per element).  The
+// host takes these instances only for d = 64 and c in [2^-4, 1], where the
+// product can neither overflow binary16 nor fall far into its subnormals.
+struct TrF16Scaled : TrF16 {};
+template <class Tr>
+constexpr bool kScaledQ = std::is_same<Tr, TrF16Scaled>::value;
+
 }  // namespace
+
+// Binary16 at d = 64 with Q pre-multiplied by p.c (defined in the object
+// built with FA_FWD_PART 3; taken without dropout when p.c lies in [2^-4, 1]).
+hipError_t launch_fwd_f16_scaled(bool causal, const FwdParams& p, hipStream_t stream);
 
 // The kernel template has external linkage so that every instantiation's
 // host-side launch stub is emitted.
@@ -95,11 +113,18 @@ struct Shape {
 template <class Tr, int D, bool CAUSAL, int QW, int NW, int BC, int SCHED, int WPE, bool DROP>
 __global__ __launch_bounds__(NW * 64, WPE) void fa_fwd_kernel(FwdParams p) {
   constexpr bool PP = SCHED == 1;
+  // Q pre-multiplied by c, and each score accumulator started at minus its
+  // row's reference: the matrix instructions then deliver S*c - m and the
+  // softmax needs no fma per score (d = 64, where vector work bounds the
+  // kernel; at d = 128 the extra register block measured slower).
+  constexpr bool kPS = kScaledQ<Tr> && D == 64 && !DROP;
   // Row sums of binary16 probabilities from the packed pairs only where
   // several independent waves of a SIMD run their softmax at once (plain
-  // schedule, no causal mask): measured faster there, slower in the lone
-  // softmax wave of the ping-pong schedule and with the causal mask.
-  constexpr bool kPackedSum = !Tr::kPvBf16 && !PP && !CAUSAL;
+  // schedule): measured faster there, slower in the lone softmax wave of the
+  // ping-pong schedule, and slower with the causal mask unless Q is
+  // pre-scaled (there they also keep the four-wave kernel within its
+  // registers).
+  constexpr bool kPackedSum = !Tr::kPvBf16 && !PP && (!CAUSAL || kPS);
   static_assert(!PP || NW == 8 || NW == 16, "the ping-pong schedule splits the waves into two groups that each hold NW/8 waves of every SIMD");
   using S = Shape<Tr, D, QW, NW, BC>;
   constexpr bool kBf = Tr::kPvBf16;
@@ -195,6 +220,16 @@ __global__ __launch_bounds__(NW * 64, WPE) void fa_fwd_kernel(FwdParams p) {
           u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rq, rowoff + (16 * s + 8 * half) * 2, 0, 0);
 #pragma unroll
           for (int e = 0; e < 4; ++e) x[e] = (x[e] ^ p.q_xor) & p.q_and;
+          if constexpr (kPS) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              // copied out first: this compiler's __builtin_bit_cast of a
+              // vector-element expression reads element 0
+              const u32 w = x[e];
+              const f32x2 f = __builtin_convertvector(__builtin_bit_cast(f16x2, w), f32x2);
+              x[e] = pack_p<false>(f[0] * p.c, f[1] * p.c);
+            }
+          }
           if (kQ1Lds && qb == 1)
             *reinterpret_cast<u32x4*>(lds_q1 + q1base + 32 * s) = x;
           else
@@ -274,6 +309,19 @@ __global__ __launch_bounds__(NW * 64, WPE) void fa_fwd_kernel(FwdParams p) {
       lsum[qb] = 0.f;
     }
     const float c = p.c;
+    // The reference a row's scores are taken against (0 before the first),
+    // and the accumulator start of a score block: minus that reference when Q
+    // is pre-scaled, else 0.
+    auto ref_off = [&](int qb) __attribute__((always_inline)) { return mref[qb] == -INFINITY ? 0.f : mref[qb]; };
+    auto qk_init = [&](int qb) __attribute__((always_inline)) {
+      f32x16 r{};
+      if constexpr (kPS) {
+        const float nb = -ref_off(qb);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) r[i] = nb;
+      }
+      return r;
+    };
 
     // Scores of the tile between its matrix phase and its softmax phase, and
     // probabilities between the softmax phase and the next matrix phase.
@@ -316,7 +364,7 @@ __global__ __launch_bounds__(NW * 64, WPE) void fa_fwd_kernel(FwdParams p) {
 #pragma unroll
       for (int kb = 0; kb < S::kKB; ++kb) {
 #pragma unroll
-        for (int qb = 0; qb < S::kQB; ++qb) dst[kb][qb] = f32x16{};
+        for (int qb = 0; qb < S::kQB; ++qb) dst[kb][qb] = qk_init(qb);
 #pragma unroll
         for (int s = 0; s < S::kQSteps; ++s)
 #pragma unroll
@@ -356,8 +404,9 @@ __global__ __launch_bounds__(NW * 64, WPE) void fa_fwd_kernel(FwdParams p) {
 
     // ---- online softmax with lazy rescaling: row maxima, then (rarely) a new
     // reference maximum with O and l rescaled.  Reductions use independent
-    // partial results so that no long dependency chain forms.
-    auto max_rescale = [&](SArr& sc) __attribute__((always_inline)) {
+    // partial results so that no long dependency chain forms.  mq: the
+    // references the scores were formed against (pre-scaled Q).
+    auto max_rescale = [&](SArr& sc, const float (&mq)[S::kQB]) __attribute__((always_inline)) {
       float mx[S::kQB];
       bool grow = false;
 #pragma unroll
@@ -371,7 +420,7 @@ __global__ __launch_bounds__(NW * 64, WPE) void fa_fwd_kernel(FwdParams p) {
             part[r / 2 & 1] = __builtin_elementwise_maximum(
                 part[r / 2 & 1], __builtin_elementwise_maximum(sc[kb][qb][r], sc[kb][qb][r + 1]));
         const float m = __builtin_elementwise_maximum(part[0], part[1]);
-        mx[qb] = halves_max(m) * c;
+        mx[qb] = kPS ? halves_max(m) + mq[qb] : halves_max(m) * c;
         grow |= mx[qb] > mref[qb] + kRescaleThreshold;
       }
       if (__builtin_amdgcn_ballot_w64(grow) != 0) {  // some row of the wave needs a new reference
@@ -387,17 +436,20 @@ __global__ __launch_bounds__(NW * 64, WPE) void fa_fwd_kernel(FwdParams p) {
       }
     };
 
-    // ---- probabilities P = exp2(S*c - m) as 16-bit pairs, row sums.  With
+    // ---- probabilities P = exp2(S*c - m) as 16-bit pairs, row sums (spec:
+    // the scores were formed against the current references).  With
     // dropout, one Philox call per lane and 32-key block gives the 16 bytes of
     // the lane's 16 scores: element r of the accumulator (key 8*(r/4) +
     // 4*half + r%4 of the block) takes byte r, i.e. bits 8*(r%4).. of word r/4.
     // The counter is (2 * block + half, query row, slice, offset).  Dropped
     // probabilities are zeroed in the P operand only: the row sum (and so the
     // normaliser and lse) is that of the whole row.
-    auto exp_tile = [&](int kt, SArr& sc, float (&tsum)[S::kQB]) __attribute__((always_inline)) {
+    auto exp_tile = [&](int kt, SArr& sc, float (&tsum)[S::kQB], const float (&mq)[S::kQB], bool spec)
+                        __attribute__((always_inline)) {
 #pragma unroll
       for (int qb = 0; qb < S::kQB; ++qb) {
-        const float mb = mref[qb] == -INFINITY ? 0.f : mref[qb];
+        const float mb = ref_off(qb);
+        const float sh = mq[qb] - mb;  // pre-scaled Q: from the scores' reference to the current one
         float rs[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < S::kKB; ++kb) {
@@ -409,8 +461,9 @@ __global__ __launch_bounds__(NW * 64, WPE) void fa_fwd_kernel(FwdParams p) {
           for (int t = 0; t < 2; ++t)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][qb][8 * t + 2 * e], c, -mb));
-              const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][qb][8 * t + 2 * e + 1], c, -mb));
+              const float s0 = sc[kb][qb][8 * t + 2 * e], s1 = sc[kb][qb][8 * t + 2 * e + 1];
+              const float p0 = __builtin_amdgcn_exp2f(kPS ? (spec ? s0 : s0 + sh) : __builtin_fmaf(s0, c, -mb));
+              const float p1 = __builtin_amdgcn_exp2f(kPS ? (spec ? s1 : s1 + sh) : __builtin_fmaf(s1, c, -mb));
               const u32 w = pack_p<kBf>(p0, p1);
               if constexpr (DROP) {
                 // elements 8t+2e and 8t+2e+1: word 2t + e/2, bytes 2*(e%2) and 2*(e%2)+1
@@ -444,10 +497,12 @@ __global__ __launch_bounds__(NW * 64, WPE) void fa_fwd_kernel(FwdParams p) {
     // its rows).  Dropout tiles always take the maxima first.
     auto softmax = [&](int kt) __attribute__((always_inline)) {
       mask_tile(kt, sacc);
-      float tsum[S::kQB];
+      float tsum[S::kQB], mq[S::kQB];
+#pragma unroll
+      for (int qb = 0; qb < S::kQB; ++qb) mq[qb] = ref_off(qb);
       if constexpr (!DROP) {
         if (down ? (ktile(kt) + 1) * BC <= qw0 : kt > 0) {
-          exp_tile(kt, sacc, tsum);
+          exp_tile(kt, sacc, tsum, mq, true);
           bool redo = false;
 #pragma unroll
           for (int qb = 0; qb < S::kQB; ++qb) redo |= !(tsum[qb] <= kSpeculativeSumLimit);
@@ -458,8 +513,8 @@ __global__ __launch_bounds__(NW * 64, WPE) void fa_fwd_kernel(FwdParams p) {
           }
         }
       }
-      max_rescale(sacc);
-      exp_tile(kt, sacc, tsum);
+      max_rescale(sacc, mq);
+      exp_tile(kt, sacc, tsum, mq, false);
 #pragma unroll
       for (int qb = 0; qb < S::kQB; ++qb) lsum[qb] += tsum[qb];
     };
@@ -535,7 +590,7 @@ __global__ __launch_bounds__(NW * 64, WPE) void fa_fwd_kernel(FwdParams p) {
 #pragma unroll
       for (int kb = 0; kb < S::kKB; ++kb) {
 #pragma unroll
-        for (int qb = 0; qb < S::kQB; ++qb) sacc[kb][qb] = f32x16{};
+        for (int qb = 0; qb < S::kQB; ++qb) sacc[kb][qb] = qk_init(qb);
 #pragma unroll
         for (int s = 0; s < S::kQSteps; ++s) {
           if constexpr (Tr::kFp8) {
@@ -604,7 +659,7 @@ __global__ __launch_bounds__(NW * 64, WPE) void fa_fwd_kernel(FwdParams p) {
       const int kb = i % S::kKB, st = i / S::kKB;
 #pragma unroll
       for (int qb = 0; qb < S::kQB; ++qb)
-        sacc[kb][qb] = mfma16(o.a, kQ1Lds && qb == 1 ? o.q1 : q16[qb][st], st == 0 ? f32x16{} : sacc[kb][qb], kBf);
+        sacc[kb][qb] = mfma16(o.a, kQ1Lds && qb == 1 ? o.q1 : q16[qb][st], st == 0 ? qk_init(qb) : sacc[kb][qb], kBf);
     };
     auto pv_rd = [&](const char* lv, int i) __attribute__((always_inline)) {
       return Ops{v_read16(lv, i % S::kDB, i / (2 * S::kDB), (i / S::kDB) % 2), u32x4{}};
@@ -794,6 +849,9 @@ template <class Tr>
 hipError_t dispatch_dtype(Dtype dt, int d, bool causal, const FwdParams& p, hipStream_t stream) {
   const bool drop = p.drop_t < 256;
   const int v = p.variant;
+  if constexpr (std::is_same<Tr, TrF16>::value) {
+    if (!drop && d == 64 && p.c >= 0.0625f && p.c <= 1.0f) return launch_fwd_f16_scaled(causal, p, stream);
+  }
   if constexpr (!Tr::kFp8) {
     if (drop) {
       if (d == 64)
@@ -810,8 +868,8 @@ hipError_t dispatch_dtype(Dtype dt, int d, bool causal, const FwdParams& p, hipS
 }  // namespace
 
 // The instances of one dtype per object when FA_FWD_PART is 0, 1 or 2 (the
-// build compiles this file once per dtype, side by side); all of them when it
-// is undefined.
+// build compiles this file once per dtype, side by side), the pre-scaled
+// binary16 ones when it is 3; all of them when it is undefined.
 #ifndef FA_FWD_PART
 #define FA_FWD_PART -1
 #endif
@@ -838,6 +896,12 @@ hipError_t launch_fwd_bf16(int d, bool causal, const FwdParams& p, hipStream_t s
 #if FA_FWD_PART < 0 || FA_FWD_PART == 2
 hipError_t launch_fwd_fp8(int d, bool causal, const FwdParams& p, hipStream_t stream) {
   return dispatch_dtype<TrFP8>(Dtype::FP8, d, causal, p, stream);
+}
+#endif
+#if FA_FWD_PART < 0 || FA_FWD_PART == 3
+hipError_t launch_fwd_f16_scaled(bool causal, const FwdParams& p, hipStream_t stream) {
+  return causal ? dispatch_variant<TrF16Scaled, 64, true>(p.variant, p, stream)
+                : dispatch_variant<TrF16Scaled, 64, false>(p.variant, p, stream);
 }
 #endif
 

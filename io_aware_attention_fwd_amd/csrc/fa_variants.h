@@ -45,11 +45,11 @@ inline constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 // under the SIMD's rate, so the shapes that keep more waves in their softmax
 // at once win: 32 rows per wave at four waves per SIMD.  Without a causal
 // mask, 8 such waves per workgroup (each K/V tile in LDS then serves 256 query
-// rows, half the tile loads per row of 4 waves) for binary16 and fp8 at every
-// length and for bfloat16 below 4096 rows; from 4096 rows on, bfloat16 (whose
-// row sums take twice the vector work) prefers 64-row ping-pong waves (twice
-// the matrix work per LDS operand) and fp8 the plain 64-row shape, both by a
-// few percent.  With the causal mask the 4-wave workgroups at four waves per
+// rows, half the tile loads per row of 4 waves) below 4096 rows, and for
+// binary16 below 8192; from there on 64-row ping-pong waves (twice the matrix
+// work per LDS operand) win for the 16-bit types (bfloat16, whose row sums
+// take twice the vector work, from 4096 rows; binary16, with Q pre-scaled,
+// +2 % at 8192) and the plain 64-row shape for fp8, each by a few percent.  With the causal mask the 4-wave workgroups at four waves per
 // SIMD win for every type (for fp8 by 1 to 5 % over three waves per SIMD, 512
 // to 16384 rows).  Packed batches of mixed lengths (N = the longest) keep
 // 128-row workgroups: larger ones idle most of their waves on the short
@@ -66,8 +66,8 @@ inline int default_variant(Dtype dt, int d, bool causal, int N, bool dropout, bo
   }
   if (dropout) return !causal && N >= 1024 ? 4 : 2;
   if (causal) return 1;
-  if (N >= 4096 && dt != Dtype::F16) return dt == Dtype::FP8 ? 4 : 5;
-  return 7;
+  if (dt == Dtype::FP8) return N >= 4096 ? 4 : 7;
+  return N >= (dt == Dtype::BF16 ? 4096 : 8192) ? 5 : 7;
 }
 
 inline int selected_variant(Dtype dt, int d, bool causal, int N, bool dropout, bool packed) {
