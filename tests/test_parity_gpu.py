@@ -87,8 +87,12 @@ def test_structured_closed_form(dtype, d, causal):
         assert np.abs(lse_np[0, h] - want_lse).max() <= 1e-5 * np.log(N)
 
 
+# Binary16 at d = 64 multiplies Q by scale*log2(e) in the kernel when that
+# factor lies in [2^-4, 1] (0, -0.125 and 0.5 here; a zero scale zeroes Q and
+# uses the factor 1) and otherwise keeps the factor in the softmax (1.0 and
+# 0.02): both paths against the oracle.
 @pytest.mark.parametrize("dtype", ["f16", "bf16", "fp8"])
-@pytest.mark.parametrize("scale", [0.0, -0.125, 0.5])
+@pytest.mark.parametrize("scale", [0.0, -0.125, 0.5, 1.0, 0.02])
 def test_scale_values(dtype, scale):
     print(f"[scale] {dtype} scale={scale}", flush=True)
     for causal in (False, True):
