@@ -49,9 +49,12 @@ inline constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 // binary16 below 8192; from there on 64-row ping-pong waves (twice the matrix
 // work per LDS operand) win for the 16-bit types (bfloat16, whose row sums
 // take twice the vector work, from 4096 rows; binary16, with Q pre-scaled,
-// +2 % at 8192) and the plain 64-row shape for fp8, each by a few percent.  With the causal mask the 4-wave workgroups at four waves per
-// SIMD win for every type (for fp8 by 1 to 5 % over three waves per SIMD, 512
-// to 16384 rows).  Packed batches of mixed lengths (N = the longest) keep
+// +2 % at 8192) and the plain 64-row shape for fp8, each by a few percent.
+// With the causal mask 4-wave workgroups at four waves per SIMD win for
+// bfloat16 and fp8 (for fp8 by 1 to 5 % over three waves per SIMD, 512 to
+// 16384 rows; 8 waves tie for bfloat16), and for binary16 below 4096 rows;
+// from 4096 rows binary16 (Q pre-scaled) gains 3 to 4 % with 8 waves (4096 to
+// 16384 rows).  Packed batches of mixed lengths (N = the longest) keep
 // 128-row workgroups: larger ones idle most of their waves on the short
 // sequences (lengths 256..4096: 660 against 596 TFLOP/s at d = 64, 726 against
 // 699 at d = 128).  Dropout kernels exist for the shapes listed in
@@ -65,7 +68,7 @@ inline int default_variant(Dtype dt, int d, bool causal, int N, bool dropout, bo
     return N >= 4096 ? 8 : N >= 2048 ? 0 : 3;
   }
   if (dropout) return !causal && N >= 1024 ? 4 : 2;
-  if (causal) return 1;
+  if (causal) return dt == Dtype::F16 && N >= 4096 ? 7 : 1;
   if (dt == Dtype::FP8) return N >= 4096 ? 4 : 7;
   return N >= (dt == Dtype::BF16 ? 4096 : 8192) ? 5 : 7;
 }
