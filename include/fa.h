@@ -82,6 +82,10 @@ enum {
  *            Any N is accepted: a tail shorter than a tile is masked, not padded.
  *   d        head dimension, 64 or 128.
  *   scale    multiplies Q K^T; any finite value (0 gives a uniform average).
+ *            Scores are scaled in float32, except for binary16 at d = 64 with
+ *            |scale| * log2(e) in [1/16, 1]: there Q is multiplied by that
+ *            factor and rounded to binary16 in the kernel (2^-11 relative per
+ *            element) before the product.
  *   causal   nonzero: query i sees keys 0..i only.
  *   dtype    an fa_dtype value.  FA_DTYPE_FP8_E4M3 here means descales of 1.
  *   stream   hipStream_t to enqueue on, or NULL.
